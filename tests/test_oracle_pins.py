@@ -1,0 +1,279 @@
+"""Pins for the CPU oracle: things the pages and the mathematics fix on their own.
+
+Each test would fail for a plausible slip in the oracle: a dropped or wrong
+scale, a transposed operand, a wrong GQA routing, logits instead of
+probabilities, a missing renormalisation, a wrong tie-break or sort direction.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import OracleLayer, IndexerOracle
+from synth import WORKLOADS, generate, random_inputs
+from tests import brute_force as bf
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _num(expr):
+    """Evaluate a golden-file entry: a fraction, or a small ln-expression."""
+    expr = str(expr)
+    if "ln" in expr:
+        if "*" in expr:
+            a, b = expr.split("*")
+            return float(a) * math.log(float(b[2:]))
+        return math.log(float(expr[2:]))
+    return float(Fraction(expr))
+
+
+# ----------------------------------------------------------------- golden rows
+def _worked_layer():
+    g = json.load(open(os.path.join(GOLDEN, "worked_rows.json")))
+    k = np.array([[_num(x) for x in row] for row in g["k_rows"]])[:, None, :]
+    qh = np.array(g["q_head_rows"], dtype=np.float64)
+    q = np.broadcast_to(qh, (4, 2, 4)).copy()
+    v = np.eye(4)[:, None, :]
+    return g, OracleLayer(q, k, v)
+
+
+def test_worked_rows_mass_lse_topk():
+    g, layer = _worked_layer()
+    assert layer.scale == 0.5
+    for i_s, exp in g["rows"].items():
+        i = int(i_s)
+        for kk, top in exp["top"].items():
+            r = layer.row(i, int(kk))
+            np.testing.assert_allclose(r["lse"], [_num(x) for x in exp["lse"]], atol=1e-12)
+            np.testing.assert_allclose(r["p"], [_num(x) for x in exp["mass"]], atol=1e-12)
+            assert r["units"].tolist() == top
+
+
+def test_worked_row3_outputs_and_blocks():
+    g, layer = _worked_layer()
+    exp = g["rows"]["3"]
+    r = layer.row(3, 2, dense=True)
+    np.testing.assert_allclose(r["out"], [[_num(x) for x in row] for row in exp["out_top2"]],
+                               atol=1e-12)
+    np.testing.assert_allclose(r["lse_s"], [_num(x) for x in exp["lse_top2"]], atol=1e-12)
+    np.testing.assert_allclose(r["dense_out"], [[_num(x) for x in row] for row in exp["dense_out"]],
+                               atol=1e-12)
+    rb = layer.row(3, 1, key_block=2)
+    np.testing.assert_allclose(rb["score"], [_num(x) for x in exp["block2_mass"]], atol=1e-12)
+    assert rb["units"].tolist() == exp["block2_top1"]
+    assert rb["support"].tolist() == [2, 3]
+
+
+# ---------------------------------------------------------- pages' sparsity
+def test_sparsity_matches_pages_sweep_ends():
+    g = json.load(open(os.path.join(GOLDEN, "sparsity_sweep.json")))
+    for c in g["cases"]:
+        got = 100.0 * oracle.causal_sparsity(c["n"], c["k"])
+        assert abs(got - c["sparsity_pct"]) <= g["tolerance_pct"], (c, got)
+        # the non-causal count 1 - k/N does not reproduce the printed figures
+        assert abs(100.0 * (1 - c["k"] / c["n"]) - c["sparsity_pct"]) > 1.0
+
+
+def test_sparsity_of_two_percent_budgets():
+    # 2 % budgets at 4K and 32K sit at the top of the pages' range
+    assert abs(100 * oracle.causal_sparsity(4096, 82) - 96.04) < 0.01
+    assert abs(100 * oracle.causal_sparsity(32768, 655) - 96.04) < 0.01
+    assert oracle.causal_sparsity(100, 100) == 0.0
+
+
+# ------------------------------------------------------------- brute force
+@pytest.mark.parametrize("shape", [(48, 8, 2, 16), (33, 4, 4, 8), (40, 6, 3, 32), (17, 2, 1, 64)])
+@pytest.mark.parametrize("kk", [1, 5, 12])
+def test_against_brute_force(shape, kk):
+    n, hq, hkv, d = shape
+    x = random_inputs(n, hq, hkv, d, "f32", seed=7 * n + kk, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    P, probs, logits = bf.full_mass(x["q"], x["k"], 1 / math.sqrt(d))
+    supports = []
+    for i in range(n):
+        r = layer.row(i, kk, dense=True)
+        np.testing.assert_allclose(r["p"], P[i, : i + 1], atol=1e-12, rtol=0)
+        assert abs(P[i].sum() - 1) < 1e-12
+        np.testing.assert_allclose(probs[:, i, : i + 1].sum(-1), 1.0, atol=1e-12)
+        assert r["units"].tolist() == bf.full_topk(P[i], i, kk).tolist()
+        supports.append(r["units"])
+    o_bf = bf.full_sparse_out(logits, x["v"], supports)
+    for i in range(n):
+        np.testing.assert_allclose(layer.row(i, kk)["out"], o_bf[i], atol=1e-12)
+
+
+def test_dense_against_torch_sdpa():
+    n, hq, hkv, d = 64, 8, 2, 32
+    x = random_inputs(n, hq, hkv, d, "f32", seed=3, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    q = torch.from_numpy(x["q"]).double().permute(1, 0, 2)[None]
+    k = torch.from_numpy(x["k"]).double().permute(1, 0, 2)[None].repeat_interleave(hq // hkv, 1)
+    v = torch.from_numpy(x["v"]).double().permute(1, 0, 2)[None].repeat_interleave(hq // hkv, 1)
+    mask = torch.ones(n, n, dtype=torch.bool).tril()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)[0]
+    ref = ref.permute(1, 0, 2).numpy()
+    for i in range(n):
+        np.testing.assert_allclose(layer.dense(i), ref[i], atol=1e-12)
+        # k >= i+1 keeps every key, so the sparse output is the dense one
+        r = layer.row(i, i + 1)
+        assert r["units"].tolist() == list(range(i + 1))
+        np.testing.assert_allclose(r["out"], ref[i], atol=1e-12)
+
+
+# ------------------------------------------------------------- closed forms
+def test_equal_keys_give_log_count():
+    n, hq, hkv, d = 20, 4, 2, 16
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((n, hq, d))
+    kap = rng.standard_normal((hkv, d))
+    k = np.broadcast_to(kap, (n, hkv, d)).copy()
+    v = rng.standard_normal((n, hkv, d))
+    layer = OracleLayer(q, k, v)
+    for i in range(n):
+        r = layer.row(i, 3)
+        for h in range(hq):
+            dot = sum(q[i, h, c] * kap[h // 2, c] for c in range(d))
+            assert abs(r["lse"][h] - (dot / math.sqrt(d) + math.log(i + 1))) < 1e-12
+        # all keys tie: the smallest indices win
+        assert r["units"].tolist() == list(range(min(3, i + 1)))
+        np.testing.assert_allclose(r["p"], 1.0 / (i + 1), atol=1e-15)
+
+
+def test_gqa_routing_contiguous_groups():
+    # KV head 1 carries zero keys: only heads 2,3 (g = h // 2) see flat logits
+    n, hq, hkv, d = 12, 4, 2, 8
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    k[:, 1, :] = 0.0
+    v = rng.standard_normal((n, hkv, d))
+    layer = OracleLayer(q, k, v)
+    for i in range(1, n):
+        lse = layer.row(i, 2)["lse"]
+        np.testing.assert_allclose(lse[2:], math.log(i + 1), atol=1e-12)
+        assert np.all(np.abs(lse[:2] - math.log(i + 1)) > 1e-6)
+    assert [oracle.kv_head(h, 4, 2) for h in range(4)] == [0, 0, 1, 1]
+
+
+def test_single_head_topk_is_topk_of_logits():
+    n, d = 64, 16
+    x = random_inputs(n, 1, 1, d, "f32", seed=9)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in range(n):
+        raw = [float(np.dot(x["q"][i, 0].astype(np.float64), x["k"][j, 0].astype(np.float64)))
+               for j in range(i + 1)]
+        want = sorted(sorted(range(i + 1), key=lambda j: -raw[j])[:7])
+        assert layer.row(i, 7)["units"].tolist() == want
+
+
+def test_identical_heads_reduce_to_single_head():
+    n, d = 40, 16
+    x = random_inputs(n, 1, 1, d, "f32", seed=13)
+    one = OracleLayer(x["q"], x["k"], x["v"])
+    many = OracleLayer(np.repeat(x["q"], 4, axis=1), x["k"], x["v"])
+    for i in range(n):
+        a, b = one.row(i, 5), many.row(i, 5)
+        assert a["units"].tolist() == b["units"].tolist()
+        np.testing.assert_allclose(a["p"], b["p"], atol=1e-15)
+
+
+def test_one_token_support_returns_its_value_row():
+    x = random_inputs(30, 4, 2, 16, "f32", seed=21)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in [0, 5, 29]:
+        for j in [0, i]:
+            out, lse_s = layer.attention_on(i, [j])
+            for h in range(4):
+                np.testing.assert_array_equal(out[h], x["v"][j, h // 2].astype(np.float64))
+                assert abs(lse_s[h] - layer.logits(i)[h, j]) < 1e-12
+
+
+def test_scaling_values_scales_output_and_weights_sum_to_one():
+    x = random_inputs(30, 4, 2, 16, "f32", seed=22)
+    a = OracleLayer(x["q"], x["k"], x["v"])
+    b = OracleLayer(x["q"], x["k"], 2.5 * x["v"].astype(np.float64))
+    ones = OracleLayer(x["q"], x["k"], np.ones_like(x["v"]))
+    for i in [3, 17, 29]:
+        np.testing.assert_allclose(b.row(i, 4)["out"], 2.5 * a.row(i, 4)["out"], atol=1e-12)
+        np.testing.assert_allclose(ones.row(i, 4)["out"], 1.0, atol=1e-12)
+
+
+def test_nesting_causality_and_capture_bound():
+    x = random_inputs(200, 8, 2, 32, "f32", seed=23, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in range(0, 200, 7):
+        prev = set()
+        for kk in (4, 16, 64):
+            r = layer.row(i, kk)
+            s = set(r["units"].tolist())
+            assert prev <= s
+            assert max(s) <= i and len(s) == min(kk, i + 1)
+            assert r["captured"] >= min(kk, i + 1) / (i + 1) - 1e-12
+            prev = s
+
+
+def test_needles_are_selected_on_tiny_workload():
+    w = WORKLOADS["tiny_fp32_512"]
+    x = generate(w)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    owners = x["owner"]
+    hits = 0
+    for j in np.nonzero(owners >= 0)[0]:
+        i = int(owners[j])
+        assert j in set(layer.row(i, w.k)["units"].tolist()), (i, j)
+        hits += 1
+    assert hits > 300
+
+
+# -------------------------------------------------------------- key blocks
+def test_block_size_one_is_token_support():
+    x = random_inputs(50, 4, 2, 16, "f32", seed=31)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in range(0, 50, 3):
+        a, b = layer.row(i, 6), layer.row(i, 6, key_block=1)
+        assert a["units"].tolist() == b["units"].tolist()
+
+
+def test_block_masses_sum_to_one_and_clip_causally():
+    x = random_inputs(100, 4, 2, 16, "f32", seed=32)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in [0, 9, 63, 64, 70, 99]:
+        r = layer.row(i, 2, key_block=8)
+        assert abs(r["score"].sum() - 1) < 1e-12
+        assert r["score"].shape[0] == i // 8 + 1
+        assert r["support"].max() <= i
+        manual = [sum(r["p"][j] for j in range(b * 8, min(b * 8 + 8, i + 1)))
+                  for b in range(i // 8 + 1)]
+        np.testing.assert_allclose(r["score"], manual, atol=1e-15)
+
+
+def test_indexer_zero_query_ties_by_block_size():
+    n, di, blk = 300, 64, 64
+    rng = np.random.default_rng(41)
+    qi = np.zeros((n, di))
+    ki = rng.standard_normal((n, di))
+    ix = IndexerOracle(qi, ki)
+    for i in [0, 63, 64, 200, 299]:
+        r = ix.row(i, 2, blk)
+        sizes = np.array([min(blk, i + 1 - b * blk) for b in range(i // blk + 1)])
+        np.testing.assert_allclose(r["score"], sizes / (i + 1), atol=1e-15)
+        full = np.nonzero(sizes == blk)[0]
+        if full.size >= 2 and sizes.size > 2:
+            assert r["units"].tolist() == [0, 1]
+
+
+def test_indexer_equals_single_head_oracle():
+    n, di = 150, 64
+    x = random_inputs(n, 1, 1, di, "bf16", seed=43)
+    ix = IndexerOracle(x["q"][:, 0], x["k"][:, 0])
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in range(0, n, 11):
+        a, b = ix.row(i, 2, 16), layer.row(i, 2, key_block=16)
+        assert a["units"].tolist() == b["units"].tolist()
+        np.testing.assert_allclose(a["score"], b["score"], atol=1e-14)
