@@ -1,0 +1,184 @@
+/*
+ * amtk.h - C ABI of the attention-mass top-k oracle library (libamtk.so) for
+ * long-context causal prefill of full/GQA attention layers on gfx950.
+ *
+ * Method: "How Much Dense Attention is Necessary? Oracle-Guided Sparse
+ * Prefill for Full/GQA Layers in Hybrid Long-Context Models" (arXiv
+ * 2606.07703). Citations below name two pages about it:
+ *   [Abstract] the authors' abstract (searcharxiv.org page);
+ *   [TB x.y]   the gist.science page, "Technischer Bericht", section x.y.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are DEVICE pointers owned by the caller, row-major, contiguous,
+ *    16-byte aligned. Q is [n][hq][d], K and V are [n][hkv][d] (token major:
+ *    one token's keys for all KV heads are hkv*d contiguous elements).
+ *    Q, K, V share one element type (amtk_attn_desc.dtype).
+ *  - Query head h reads KV head h / (hq/hkv) (contiguous GQA groups).
+ *  - Row i attends to keys j <= i (causal prefill).
+ *  - Logits are scale * <Q[i,h], K[j,g]>; scale <= 0 selects 1/sqrt(d).
+ *  - Every call validates its arguments on the host first and launches
+ *    nothing when a check fails. Work is enqueued asynchronously on `stream`
+ *    (a hipStream_t; NULL = the null stream). The library never allocates,
+ *    frees or synchronises; it keeps no mutable global state, so calls on
+ *    different streams with disjoint outputs and workspaces may overlap.
+ *  - Every element of every output is written (-1 / 0 padding included).
+ *  - Return value: AMTK_OK or a negative AMTK_E_* code (see amtk_strerror).
+ */
+#ifndef AMTK_H
+#define AMTK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AMTK_OK 0
+#define AMTK_E_INVALID (-1)     /* null pointer, bad size, inconsistent arguments */
+#define AMTK_E_UNSUPPORTED (-2) /* well-formed but outside what the kernels cover */
+#define AMTK_E_WORKSPACE (-3)   /* workspace smaller than the *_workspace query says */
+#define AMTK_E_HIP (-4)         /* a HIP launch failed; see amtk_last_hip_error */
+
+#define AMTK_BF16 0
+#define AMTK_F32 1
+
+/* One GQA attention layer in prefill. */
+typedef struct {
+  int64_t n;      /* tokens (rows), 1 <= n < 2^31 */
+  int32_t hq;     /* query heads */
+  int32_t hkv;    /* KV heads; hq % hkv == 0 */
+  int32_t d;      /* head dim: 64 or 128 */
+  int32_t dtype;  /* AMTK_BF16 or AMTK_F32 (arithmetic is fp32 either way) */
+  int32_t causal; /* must be 1: the method is defined for causal prefill */
+  float scale;    /* softmax temperature on the logits; <= 0 means 1/sqrt(d) */
+} amtk_attn_desc;
+
+/* Support granularity and budget ([TB 2.1]: budget k and support granularity;
+ * [TB 2.2]: k stays adjustable at inference). */
+typedef struct {
+  int32_t k;             /* budget, in key_block units, 1 <= k <= 8192 */
+  int32_t key_block;     /* 1 = token support, 64 = aligned 64-token key blocks */
+  int32_t query_block;   /* queries sharing one support (b_sel); must be 1 */
+  int32_t candidate_cap; /* candidates kept per row by the streaming filter;
+                            0 = automatic. Rows that exceed it are recomputed
+                            densely, so any value >= 1 gives the same result. */
+} amtk_support_desc;
+
+/* Bytes of device workspace topk_support / oracle_prefill need for these
+ * shapes (written to *bytes). Returns AMTK_OK or a validation error. */
+int amtk_topk_workspace(const amtk_attn_desc* attn, const amtk_support_desc* sup, size_t* bytes);
+
+/*
+ * topk_support - the attention-mass top-k oracle's support selection.
+ * [TB 2.1], [Abstract]: for every query row i the per-head causal softmax
+ * p_h(i,j) = exp(s_h(i,j) - LSE_h(i)) is averaged over all hq heads,
+ * P_i(j) = (1/hq) sum_h p_h(i,j), and the top-k units of P_i are kept.
+ * key_block = 64 ranks aligned key blocks by M_i(b) = sum of P_i(j) over the
+ * block's keys j <= i. Units are ranked by mass descending, then id ascending.
+ * A row with at most k visible units keeps all of them.
+ *
+ * Two passes over the causal score matrix (per-head LSE, then mass + streaming
+ * threshold filter) and an exact select; the n x n mass is never stored.
+ *
+ * q, k      : inputs as described above.
+ * idx       : OUT [n][k] int32, row i's selected unit ids (token ids, or key
+ *             block ids when key_block = 64) ascending, then -1 padding.
+ * count     : OUT [n] int32, number of selected units = min(k, visible units).
+ * mass      : OUT [n][k] fp32 mass of each selected unit (0 padding), or NULL.
+ * lse       : OUT [hq][n] fp32 per-head dense log-sum-exp (natural log), or NULL.
+ * ws        : device workspace of ws_bytes >= amtk_topk_workspace(); its
+ *             contents on entry are ignored; it is owned by the caller and
+ *             must not be shared by calls that run concurrently.
+ */
+int topk_support(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
+                 const void* k, int32_t* idx, int32_t* count, float* mass, float* lse, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * topk_support_stage - one stage of topk_support, for callers that time or
+ * schedule the stages separately. Calling stages 1, 2, 3 in that order on
+ * one stream with the same arguments and workspace is exactly topk_support:
+ *   stage 1: per-head dense log-sum-exp pass (writes lse, or the workspace's
+ *            copy when lse is NULL);
+ *   stage 2: head-averaged mass pass with the streaming top-k filter
+ *            (candidate pool in the workspace);
+ *   stage 3: exact select from the pool (rows whose pool overflowed are
+ *            recomputed densely), writes idx, count and mass.
+ * Stages 2 and 3 read what the earlier stages left in ws (and lse).
+ */
+int topk_support_stage(const amtk_attn_desc* attn, const amtk_support_desc* sup, int32_t stage,
+                       const void* q, const void* k, int32_t* idx, int32_t* count, float* mass,
+                       float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_attn - attention recomputed on each row's support only.
+ * [TB 2.1], [TB 2.2], [Abstract]: O_i[h] = sum_{j in S_i}
+ * softmax_{S_i}(s_h(i,j)) V[j, g(h)], the softmax renormalised over S_i.
+ * S_i is given by idx/count in the layout topk_support writes:
+ * key_block = 1: idx[i][0..count[i]) are token ids; key_block = 64: they are
+ * key block ids, expanded to tokens b*64 .. b*64+63 and clipped to j <= i.
+ * Negative ids and tokens j > i are skipped; count[i] is clamped to
+ * [0, max_units]. A row with an empty support gets O = 0 and LSE = -inf.
+ *
+ * idx       : [n][max_units] int32 (device); count: [n] int32 (device).
+ * o         : OUT [n][hq][d] fp32.
+ * lse_sparse: OUT [hq][n] fp32 log-sum-exp over the support, or NULL.
+ */
+int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units, const void* q,
+                const void* k, const void* v, const int32_t* idx, const int32_t* count, float* o,
+                float* lse_sparse, void* stream);
+
+/*
+ * oracle_prefill - topk_support followed by sparse_attn on the same stream:
+ * the oracle's full per-layer step (dense mass -> top-k support -> sparse
+ * recompute with the original Q/K/V), [TB 2.1], [Abstract].
+ * Arguments as in the two calls above; idx and count are required outputs.
+ */
+int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
+                   const void* k, const void* v, float* o, int32_t* idx, int32_t* count,
+                   float* mass, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of indexer_topk for these shapes. */
+int amtk_indexer_workspace(int64_t n, int32_t d_idx, int32_t dtype,
+                           const amtk_support_desc* sup, size_t* bytes);
+
+/*
+ * indexer_topk - head-collapsed indexer scoring and top-k.
+ * [TB 2.2], [Abstract]: one shared score per key replaces per-head scores,
+ * s(i,j) = scale * <q_idx[i], k_idx[j]>; P_idx = causal softmax over j <= i;
+ * units are tokens (key_block = 1) or aligned 64-token key blocks ranked by
+ * their summed P_idx (key_block = 64); the top-k units feed sparse_attn.
+ *
+ * q_idx, k_idx: [n][d_idx] device tensors, d_idx = 64 or 128.
+ * scale <= 0 selects 1/sqrt(d_idx).
+ * idx/count/mass/ws as in topk_support.
+ */
+int indexer_topk(int64_t n, int32_t d_idx, int32_t dtype, float scale,
+                 const amtk_support_desc* sup, const void* q_idx, const void* k_idx,
+                 int32_t* idx, int32_t* count, float* mass, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Message for an AMTK_* code. Never NULL. */
+const char* amtk_strerror(int code);
+
+/* The hipError_t of the most recent AMTK_E_HIP returned on this thread. */
+int amtk_last_hip_error(void);
+
+/*
+ * amtk_pool_stats - diagnostics of the last topk_support / indexer_topk run
+ * that used workspace `ws` (same descriptors). Copies the per-row candidate
+ * counts back and reports the largest count, the number of rows whose pool
+ * overflowed the capacity (recomputed densely), and the capacity itself.
+ * SYNCHRONOUS: waits for `stream`. For tests and tuning only.
+ */
+int amtk_pool_stats(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* ws,
+                    size_t ws_bytes, int64_t* max_candidates, int64_t* overflow_rows,
+                    int64_t* capacity, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AMTK_H */

@@ -1,0 +1,283 @@
+// C-ABI entry points of libamtk.so (declared in include/amtk.h).
+//
+// Host-side only: validates descriptors and pointers, carves the caller's
+// workspace, and enqueues the kernels on the caller's stream. Nothing here
+// allocates device memory or synchronises (except amtk_pool_stats, which is
+// documented as a synchronous diagnostic).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "amtk.h"
+#include "kernels.h"
+
+using amtk::CandidatePool;
+using amtk::LayerShape;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return AMTK_E_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_attn(const amtk_attn_desc* a, LayerShape* s) {
+  if (!a) return AMTK_E_INVALID;
+  if (a->n < 1 || a->n >= (int64_t)1 << 31) return AMTK_E_INVALID;
+  if (a->hq < 1 || a->hkv < 1 || a->d < 1) return AMTK_E_INVALID;
+  if (a->hq % a->hkv) return AMTK_E_INVALID;
+  if (a->dtype != AMTK_BF16 && a->dtype != AMTK_F32) return AMTK_E_INVALID;
+  if (std::isnan(a->scale) || std::isinf(a->scale)) return AMTK_E_INVALID;
+  if (a->causal != 1) return AMTK_E_UNSUPPORTED;
+  if (a->d != 64 && a->d != 128) return AMTK_E_UNSUPPORTED;
+  s->n = (int)a->n;
+  s->hq = a->hq;
+  s->hkv = a->hkv;
+  s->d = a->d;
+  s->dtype = a->dtype;
+  s->scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->d);
+  return AMTK_OK;
+}
+
+int check_support(const amtk_support_desc* sp) {
+  if (!sp) return AMTK_E_INVALID;
+  if (sp->k < 1 || sp->candidate_cap < 0) return AMTK_E_INVALID;
+  if (sp->k > amtk::kMaxBudget) return AMTK_E_UNSUPPORTED;
+  if (sp->key_block != 1 && sp->key_block != 64) return AMTK_E_UNSUPPORTED;
+  if (sp->query_block != 1) return AMTK_E_UNSUPPORTED;
+  return AMTK_OK;
+}
+
+struct Layout {
+  size_t cand, count, bin, lse, ovf_count, ovf_list, scratch, total;
+  int cap, units_max;
+};
+
+Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
+  Layout L;
+  const size_t n = (size_t)s.n;
+  L.units_max = sp.key_block == 1 ? s.n : (s.n - 1) / sp.key_block + 1;
+  int cap = sp.candidate_cap > 0 ? sp.candidate_cap
+                                 : (8 * sp.k > 4096 ? 8 * sp.k : 4096);
+  if (cap > L.units_max) cap = L.units_max;
+  L.cap = cap;
+  size_t off = 0;
+  L.cand = off;       off = round_up(off + n * (size_t)cap * sizeof(uint2));
+  L.count = off;      off = round_up(off + n * sizeof(int));
+  L.bin = off;        off = round_up(off + n * sizeof(int));
+  L.lse = off;        off = round_up(off + (size_t)s.hq * n * sizeof(float));
+  L.ovf_count = off;  off = round_up(off + sizeof(int));
+  L.ovf_list = off;   off = round_up(off + n * sizeof(int));
+  L.scratch = off;    off = round_up(off + (size_t)amtk::kFallbackSlots * L.units_max * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+CandidatePool pool_of(void* ws, const Layout& L) {
+  unsigned char* b = static_cast<unsigned char*>(ws);
+  CandidatePool p;
+  p.cand = reinterpret_cast<uint2*>(b + L.cand);
+  p.count = reinterpret_cast<int*>(b + L.count);
+  p.bin = reinterpret_cast<int*>(b + L.bin);
+  p.ovf_count = reinterpret_cast<int*>(b + L.ovf_count);
+  p.ovf_list = reinterpret_cast<int*>(b + L.ovf_list);
+  p.scratch = reinterpret_cast<float*>(b + L.scratch);
+  p.cap = L.cap;
+  p.slots = amtk::kFallbackSlots;
+  return p;
+}
+
+// Shared body of topk_support, topk_support_stage and indexer_topk
+// (validated descriptors). stage 0 runs all three stages.
+int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const void* q,
+             const void* k, int32_t* idx, int32_t* count, float* mass, float* lse, void* ws,
+             size_t ws_bytes, hipStream_t stream) {
+  if (!amtk::pass_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  if (stage < 0 || stage > 3) return AMTK_E_INVALID;
+  if (!q || !k || !ws || ((stage == 0 || stage == 3) && (!idx || !count))) return AMTK_E_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
+      !aligned(ws, 256) || (mass && !aligned(mass, 4)) || (lse && !aligned(lse, 4)))
+    return AMTK_E_INVALID;
+  const Layout L = layout(s, sp);
+  if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
+  const CandidatePool pool = pool_of(ws, L);
+  float* lse_buf = lse ? lse : reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + L.lse);
+  hipError_t e = hipSuccess;
+  if (stage == 0 || stage == 1) {
+    e = amtk::launch_pass1_lse(s, q, k, lse_buf, pool.ovf_count, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (stage == 0 || stage == 2) {
+    e = amtk::launch_pass2_filter(s, sp.key_block, sp.k, q, k, lse_buf, pool, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (stage == 0 || stage == 3) {
+    e = amtk::launch_select(s, sp.key_block, sp.k, q, k, lse_buf, pool, idx, count, mass, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return AMTK_OK;
+}
+
+int indexer_shape(int64_t n, int32_t d_idx, int32_t dtype, float scale, LayerShape* s) {
+  amtk_attn_desc a;
+  a.n = n;
+  a.hq = 1;
+  a.hkv = 1;
+  a.d = d_idx;
+  a.dtype = dtype;
+  a.causal = 1;
+  a.scale = scale;
+  return check_attn(&a, s);
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int amtk_topk_workspace(const amtk_attn_desc* attn, const amtk_support_desc* sup, size_t* bytes) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  if (!bytes) return AMTK_E_INVALID;
+  if (!amtk::pass_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  *bytes = layout(s, *sup).total;
+  return AMTK_OK;
+}
+
+int topk_support(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
+                 const void* k, int32_t* idx, int32_t* count, float* mass, float* lse, void* ws,
+                 size_t ws_bytes, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  return run_topk(s, *sup, 0, q, k, idx, count, mass, lse, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+int topk_support_stage(const amtk_attn_desc* attn, const amtk_support_desc* sup, int32_t stage,
+                       const void* q, const void* k, int32_t* idx, int32_t* count, float* mass,
+                       float* lse, void* ws, size_t ws_bytes, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  if (stage < 1 || stage > 3) return AMTK_E_INVALID;
+  return run_topk(s, *sup, stage, q, k, idx, count, mass, lse, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units, const void* q,
+                const void* k, const void* v, const int32_t* idx, const int32_t* count, float* o,
+                float* lse_sparse, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if (max_units < 1) return AMTK_E_INVALID;
+  if (key_block != 1 && key_block != 64) return AMTK_E_UNSUPPORTED;
+  if (!amtk::sparse_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  if (!q || !k || !v || !idx || !count || !o) return AMTK_E_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
+      !aligned(count, 4) || !aligned(o, 16) || (lse_sparse && !aligned(lse_sparse, 4)))
+    return AMTK_E_INVALID;
+  hipError_t e = amtk::launch_sparse_attn(s, key_block, max_units, q, k, v, idx, count, o,
+                                          lse_sparse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
+int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
+                   const void* k, const void* v, float* o, int32_t* idx, int32_t* count,
+                   float* mass, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  if (!amtk::sparse_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  if (!v || !o) return AMTK_E_INVALID;
+  if (!aligned(v, 16) || !aligned(o, 16)) return AMTK_E_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = run_topk(s, *sup, 0, q, k, idx, count, mass, lse, ws, ws_bytes, st);
+  if (rc) return rc;
+  hipError_t e =
+      amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o, nullptr, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
+int amtk_indexer_workspace(int64_t n, int32_t d_idx, int32_t dtype,
+                           const amtk_support_desc* sup, size_t* bytes) {
+  LayerShape s;
+  int rc = indexer_shape(n, d_idx, dtype, 0.f, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  if (!bytes) return AMTK_E_INVALID;
+  *bytes = layout(s, *sup).total;
+  return AMTK_OK;
+}
+
+int indexer_topk(int64_t n, int32_t d_idx, int32_t dtype, float scale,
+                 const amtk_support_desc* sup, const void* q_idx, const void* k_idx,
+                 int32_t* idx, int32_t* count, float* mass, void* ws, size_t ws_bytes,
+                 void* stream) {
+  LayerShape s;
+  int rc = indexer_shape(n, d_idx, dtype, scale, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  return run_topk(s, *sup, 0, q_idx, k_idx, idx, count, mass, nullptr, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+const char* amtk_strerror(int code) {
+  switch (code) {
+    case AMTK_OK: return "success";
+    case AMTK_E_INVALID: return "invalid argument (null pointer, size, alignment or inconsistent shapes)";
+    case AMTK_E_UNSUPPORTED: return "unsupported configuration (dtype, head_dim, group size, budget, granularity or non-causal)";
+    case AMTK_E_WORKSPACE: return "workspace too small";
+    case AMTK_E_HIP: return "HIP launch failed (see amtk_last_hip_error)";
+  }
+  return "unknown error code";
+}
+
+int amtk_last_hip_error(void) { return g_last_hip; }
+
+int amtk_pool_stats(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* ws,
+                    size_t ws_bytes, int64_t* max_candidates, int64_t* overflow_rows,
+                    int64_t* capacity, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if ((rc = check_support(sup))) return rc;
+  if (!ws || !max_candidates || !overflow_rows || !capacity) return AMTK_E_INVALID;
+  const Layout L = layout(s, *sup);
+  if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<int> counts((size_t)s.n);
+  int ovf = 0;
+  const unsigned char* b = static_cast<const unsigned char*>(ws);
+  hipError_t e = hipMemcpyAsync(counts.data(), b + L.count, counts.size() * sizeof(int),
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(&ovf, b + L.ovf_count, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  int64_t mx = 0;
+  for (int c : counts) mx = c > mx ? c : mx;
+  *max_candidates = mx;
+  *overflow_rows = ovf;
+  *capacity = L.cap;
+  return AMTK_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

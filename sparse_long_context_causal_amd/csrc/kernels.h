@@ -1,0 +1,63 @@
+// Internal launchers behind the C-ABI (not exported). Every launcher assumes
+// its arguments were validated by the API layer and only enqueues work on
+// `stream`; none allocates, frees or synchronises.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace amtk {
+
+enum ElemType { kBF16 = 0, kF32 = 1 };
+
+struct LayerShape {
+  int n;        // tokens
+  int hq;       // query heads
+  int hkv;      // KV heads
+  int d;        // head dim
+  int dtype;    // ElemType
+  float scale;  // softmax temperature on the logits
+};
+
+// Candidate pool produced by pass 2 and consumed by the select kernels.
+struct CandidatePool {
+  uint2* cand;      // [n][cap] (mass bits, unit id)
+  int* count;       // [n] candidates seen (may exceed cap: overflow)
+  int* bin;         // [n] final threshold bin (diagnostic)
+  int* ovf_count;   // [1] rows whose pool overflowed
+  int* ovf_list;    // [n] their row ids
+  float* scratch;   // [slots][units_max] dense rows for the overflow path
+  int cap;          // capacity per row
+  int slots;        // overflow rows processed concurrently
+};
+
+constexpr int kMaxBudget = 8192;      // largest k the select kernel sorts in LDS
+constexpr int kMaxQRow = 8192;        // largest Hq*d held in LDS by the overflow path
+constexpr int kFallbackSlots = 128;   // concurrent overflow rows
+
+// Per-head causal row log-sum-exp, lse[h][i] (natural log). Also zeroes
+// pool.ovf_count for the pass that follows.
+hipError_t launch_pass1_lse(const LayerShape& s, const void* q, const void* k, float* lse,
+                            int* zero_counter, hipStream_t stream);
+
+// Head-averaged mass, streaming threshold filter, candidate compaction.
+hipError_t launch_pass2_filter(const LayerShape& s, int key_block, int budget, const void* q,
+                               const void* k, const float* lse, const CandidatePool& pool,
+                               hipStream_t stream);
+
+// Exact top-k from each row's candidates (rows whose pool did not overflow),
+// then the dense recompute + select for rows that did.
+hipError_t launch_select(const LayerShape& s, int key_block, int budget, const void* q,
+                         const void* k, const float* lse, const CandidatePool& pool, int32_t* idx,
+                         int32_t* count, float* mass, hipStream_t stream);
+
+// Attention on each row's support (token ids or key blocks), fp32 output.
+hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units, const void* q,
+                              const void* k, const void* v, const int32_t* idx,
+                              const int32_t* count, float* o, float* lse_sparse,
+                              hipStream_t stream);
+
+bool pass_shape_supported(const LayerShape& s);
+bool sparse_shape_supported(const LayerShape& s);
+
+}  // namespace amtk

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI: the library loads, exports exactly what
+include/amtk.h declares, and rejects bad arguments before launching anything.
+No call here reaches a GPU: every argument set fails validation on the host.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "amtk.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_long_context_causal_amd import _abi, build
+    if not os.path.exists(_abi.LIB_PATH):
+        build.build(verbose=False)
+    return _abi.open_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("oracle_prefill", "topk_support", "sparse_attn", "indexer_topk"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from sparse_long_context_causal_amd import _abi
+    names = declared_functions()
+    assert set(names) == set(_abi.SIGNATURES), (names, sorted(_abi.SIGNATURES))
+    for n in names:
+        assert getattr(lib, n) is not None
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    # nothing else of ours leaks out
+    ours = {s for s in exported if "amtk" in s or s in names}
+    assert ours == set(names), sorted(ours - set(names))
+
+
+def test_strerror_covers_codes(lib):
+    for c in (0, -1, -2, -3, -4, -99):
+        assert lib.amtk_strerror(c)
+
+
+def _descs(n=64, hq=8, hkv=2, d=64, dtype=0, causal=1, scale=0.0, k=4, kb=1, qb=1, cap=0):
+    from sparse_long_context_causal_amd._abi import AttnDesc, SupportDesc
+    return AttnDesc(n, hq, hkv, d, dtype, causal, scale), SupportDesc(k, kb, qb, cap)
+
+
+FAKE = ctypes.c_void_p(0x100000)   # 256-aligned, never dereferenced on the host
+
+
+def _topk(lib, a, s, ws_bytes=1, q=FAKE, ws=FAKE, idx=FAKE):
+    return lib.topk_support(ctypes.byref(a) if a is not None else None, ctypes.byref(s),
+                            q, FAKE, idx, FAKE, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), -1), (dict(hq=6, hkv=4), -1), (dict(dtype=7), -1), (dict(scale=float("nan")), -1),
+    (dict(k=0), -1), (dict(cap=-1), -1),
+    (dict(causal=0), -2), (dict(d=96), -2), (dict(kb=2), -2), (dict(qb=64), -2), (dict(k=9000), -2),
+    (dict(hq=32, hkv=2), -2),          # 16 query heads per KV head
+    (dict(hkv=16, hq=16), -2),         # more KV heads than pass waves
+    (dict(dtype=1, d=128, hq=8, hkv=2), -2),   # fp32 group tile too large for registers
+])
+def test_invalid_arguments_are_rejected(lib, kw, code):
+    a, s = _descs(**kw)
+    assert _topk(lib, a, s) == code
+
+
+def test_null_and_misaligned_pointers(lib):
+    a, s = _descs()
+    assert _topk(lib, None, s) == -1
+    assert _topk(lib, a, s, q=None) == -1
+    assert _topk(lib, a, s, q=ctypes.c_void_p(0x100004)) == -1     # q not 16-byte aligned
+    assert _topk(lib, a, s, ws=ctypes.c_void_p(0x100010)) == -1    # ws not 256-byte aligned
+
+
+def test_workspace_too_small(lib):
+    a, s = _descs()
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s), ctypes.byref(need)) == 0
+    assert need.value > 0
+    assert _topk(lib, a, s, ws_bytes=need.value - 1) == -3
+
+
+def test_workspace_sizes_grow_with_n_and_cap(lib):
+    prev = 0
+    for n in (1, 33, 512, 4096):
+        a, s = _descs(n=n)
+        need = ctypes.c_size_t(0)
+        assert lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s), ctypes.byref(need)) == 0
+        assert need.value > prev
+        prev = need.value
+    a, s1 = _descs(n=4096, cap=10)
+    _, s2 = _descs(n=4096, cap=100)
+    b1, b2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s1), ctypes.byref(b1))
+    lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s2), ctypes.byref(b2))
+    assert b2.value - b1.value >= 4096 * 90 * 8
+
+
+def test_sparse_attn_validation(lib):
+    a, _ = _descs()
+    f = lib.sparse_attn
+    assert f(ctypes.byref(a), 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(ctypes.byref(a), 3, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert f(ctypes.byref(a), 1, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
+
+
+def test_indexer_validation(lib):
+    _, s = _descs(kb=64, k=16)
+    f = lib.indexer_topk
+    assert f(0, 64, 0, 0.0, ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, None) == -1
+    assert f(100, 32, 0, 0.0, ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, None) == -2
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_indexer_workspace(100, 64, 0, ctypes.byref(s), ctypes.byref(need)) == 0
+    assert f(100, 64, 0, 0.0, ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+             need.value - 1, None) == -3
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from sparse_long_context_causal_amd import _abi
+    with pytest.raises(RuntimeError):
+        _abi.open_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Index sets must match except within 1e-6 of the k-th mass; outputs on
+identical supports within 2e-3 (bf16 inputs) / 1e-5 (fp32 inputs) max abs;
+per-head LSE within 1e-4 / 1e-5; masses within 1e-7 + 2e-4 * P.
+Small shapes are compared on every row (several 32-row tiles and a ragged
+tail); the full-size workloads on the seeded oracle row samples, in the same
+launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import OracleLayer, IndexerOracle, tokens_of_blocks
+from synth import WORKLOADS, generate, random_inputs, sample_rows
+from tests.gpu_helpers import (BAND, TOL_LSE, TOL_OUT, check_outputs_on_gpu_support,
+                               check_support_rows, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_oracle_prefill(amtk, x, dtype, k, key_block=1, cap=0):
+    import torch
+    d = upload(x, dtype)
+    out, idx, count, mass, lse = amtk.oracle_prefill(d["q"], d["k"], d["v"], k, key_block,
+                                                     candidate_cap=cap)
+    torch.cuda.synchronize()
+    return {"out": out.cpu().numpy(), "idx": idx.cpu().numpy(), "count": count.cpu().numpy(),
+            "mass": mass.cpu().numpy(), "lse": lse.cpu().numpy()}
+
+
+def _full_check(amtk, x, dtype, k, key_block=1, rows=None, cap=0):
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    res = _run_oracle_prefill(amtk, x, dtype, k, key_block, cap)
+    n = x["q"].shape[0]
+    rows = np.arange(n) if rows is None else rows
+    for i in rows:
+        r = layer.row(int(i), k, key_block)
+        assert np.max(np.abs(res["lse"][:, i] - r["lse"])) <= TOL_LSE[dtype], f"lse row {i}"
+        sel = res["idx"][i][: res["count"][i]]
+        want = r["score"][sel]
+        assert np.all(np.abs(res["mass"][i][: res["count"][i]] - want) <= 1e-7 + 2e-4 * want), \
+            f"mass row {i}"
+    check_support_rows(res["idx"], res["count"], layer, rows, k, key_block)
+    check_outputs_on_gpu_support(res["out"], None, layer, rows, res["idx"], res["count"],
+                                 key_block, dtype)
+    return res, layer
+
+
+# ------------------------------------------------------------ small shapes
+@pytest.mark.parametrize("n,hq,hkv,d,dtype,k", [
+    (1, 8, 2, 64, "f32", 4),        # one token
+    (33, 8, 2, 64, "f32", 5),       # ragged second tile
+    (200, 8, 2, 64, "f32", 32),
+    (150, 32, 8, 128, "bf16", 12),
+    (300, 4, 1, 128, "bf16", 20),   # MQA
+    (130, 4, 4, 128, "bf16", 7),    # MHA (G = 1)
+    (97, 16, 8, 128, "bf16", 9),    # G = 2
+    (161, 8, 1, 64, "bf16", 11),    # G = 8, d = 64
+    (90, 4, 2, 128, "f32", 6),      # fp32, d = 128
+])
+def test_small_shapes_all_rows(gpu_lib, n, hq, hkv, d, dtype, k):
+    x = random_inputs(n, hq, hkv, d, dtype, seed=n * 7 + hq, sink=True)
+    _full_check(gpu_lib, x, dtype, k)
+
+
+def test_budget_at_least_row_length_is_dense(gpu_lib):
+    import torch
+    n = 96
+    x = random_inputs(n, 8, 2, 128, "bf16", seed=5, sink=True)
+    res = _run_oracle_prefill(gpu_lib, x, "bf16", n)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in range(n):
+        assert res["count"][i] == i + 1
+        assert res["idx"][i][: i + 1].tolist() == list(range(i + 1))
+        assert np.all(res["idx"][i][i + 1:] == -1)
+        assert np.max(np.abs(res["out"][i] - layer.dense(i))) <= TOL_OUT["bf16"]
+
+
+def test_equal_keys_tie_to_smallest_ids(gpu_lib):
+    n, hq, hkv, d = 120, 8, 2, 64
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((n, hq, d)).astype(np.float32)
+    k = np.broadcast_to(rng.standard_normal((1, hkv, d)), (n, hkv, d)).astype(np.float32).copy()
+    v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    res = _run_oracle_prefill(gpu_lib, {"q": q, "k": k, "v": v}, "f32", 10)
+    for i in range(n):
+        assert res["idx"][i][: res["count"][i]].tolist() == list(range(min(10, i + 1)))
+
+
+def test_overflow_path_gives_same_supports(gpu_lib):
+    """A tiny candidate capacity forces the dense per-row recompute."""
+    x = random_inputs(260, 8, 2, 128, "bf16", seed=11, sink=True)
+    a = _run_oracle_prefill(gpu_lib, x, "bf16", 16)
+    b = _run_oracle_prefill(gpu_lib, x, "bf16", 16, cap=17)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    check_support_rows(b["idx"], b["count"], layer, np.arange(260), 16)
+    assert np.array_equal(a["count"], b["count"])
+    same = np.mean([np.array_equal(a["idx"][i], b["idx"][i]) for i in range(260)])
+    assert same > 0.98
+    check_outputs_on_gpu_support(b["out"], None, layer, np.arange(0, 260, 7), b["idx"],
+                                 b["count"], 1, "bf16")
+
+
+def test_overflow_rows_are_reported(gpu_lib):
+    import torch
+    amtk = gpu_lib
+    x = random_inputs(300, 8, 2, 64, "bf16", seed=12)
+    d = upload(x, "bf16")
+    ad, sd = amtk.attn_desc(d["q"], d["k"]), amtk.support_desc(8, 1, 9)
+    ws = amtk.workspace(amtk.topk_workspace_bytes(ad, sd), d["q"].device)
+    amtk.topk_support(d["q"], d["k"], 8, 1, candidate_cap=9, ws=ws)
+    mx, ov, cap = amtk.pool_stats(ad, sd, ws)
+    assert cap == 9 and mx > 9 and ov > 0
+    sd2 = amtk.support_desc(8, 1, 0)
+    ws2 = amtk.workspace(amtk.topk_workspace_bytes(ad, sd2), d["q"].device)
+    amtk.topk_support(d["q"], d["k"], 8, 1, ws=ws2)
+    mx2, ov2, cap2 = amtk.pool_stats(ad, sd2, ws2)
+    assert ov2 == 0 and mx2 <= cap2
+
+
+def test_key_block_support(gpu_lib):
+    x = random_inputs(700, 8, 2, 128, "bf16", seed=21, sink=True)
+    _full_check(gpu_lib, x, "bf16", 3, key_block=64)
+
+
+def test_key_block_support_overflow_path(gpu_lib):
+    x = random_inputs(700, 8, 2, 64, "f32", seed=22, sink=True)
+    _full_check(gpu_lib, x, "f32", 2, key_block=64, cap=2)
+
+
+def test_repeatable_bitwise(gpu_lib):
+    x = random_inputs(400, 32, 8, 128, "bf16", seed=31, sink=True)
+    a = _run_oracle_prefill(gpu_lib, x, "bf16", 24)
+    for _ in range(2):
+        b = _run_oracle_prefill(gpu_lib, x, "bf16", 24)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), key
+
+
+def test_sparse_attn_given_oracle_supports(gpu_lib):
+    """K3 alone, driven by the oracle's supports (independent of K1/K2)."""
+    import torch
+    amtk = gpu_lib
+    n, k = 257, 19
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=41, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    idx = -np.ones((n, k), dtype=np.int32)
+    cnt = np.zeros(n, dtype=np.int32)
+    for i in range(n):
+        u = layer.row(i, k)["units"]
+        idx[i, : u.size] = u
+        cnt[i] = u.size
+    d = upload(x, "bf16")
+    out, lse_s = amtk.sparse_attn(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
+                                  torch.from_numpy(cnt).cuda(), 1, want_lse=True)
+    check_outputs_on_gpu_support(out.cpu().numpy(), lse_s.cpu().numpy(), layer, range(n), idx,
+                                 cnt, 1, "bf16")
+
+
+def test_sparse_attn_one_token_and_empty(gpu_lib):
+    import torch
+    amtk = gpu_lib
+    n = 40
+    x = random_inputs(n, 8, 2, 64, "f32", seed=42)
+    idx = np.full((n, 3), -1, dtype=np.int32)
+    cnt = np.ones(n, dtype=np.int32)
+    idx[:, 0] = np.arange(n) // 2
+    cnt[5] = 0
+    d = upload(x, "f32")
+    out, lse = amtk.sparse_attn(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
+                                torch.from_numpy(cnt).cuda(), 1, want_lse=True)
+    out = out.cpu().numpy()
+    for i in range(n):
+        if i == 5:
+            assert np.all(out[i] == 0) and np.all(np.isneginf(lse.cpu().numpy()[:, i]))
+            continue
+        for h in range(8):
+            np.testing.assert_array_equal(out[i, h], x["v"][i // 2, h // 4])
+
+
+# ------------------------------------------------------------ the workloads
+def _workload_check(amtk, name, rows_cap=None, n=None):
+    w = WORKLOADS[name]
+    x = generate(w, n=n)
+    rows = sample_rows(w, n=n)
+    if rows_cap is not None and rows.size > rows_cap:
+        rows = rows[np.linspace(0, rows.size - 1, rows_cap).astype(int)]
+    res, layer = _full_check(amtk, x, w.dtype, w.k, w.key_block, rows=rows)
+    # every surviving needle (owner row, key) in the checked rows is selected
+    owners = x["owner"]
+    for i in rows:
+        mine = np.nonzero(owners == i)[0]
+        sel = set(res["idx"][i][: res["count"][i]].tolist())
+        assert set(mine.tolist()) <= sel, f"row {i} lost a needle"
+    return res
+
+
+def test_workload_tiny_fp32_512_all_rows(gpu_lib):
+    _workload_check(gpu_lib, "tiny_fp32_512")
+
+
+def test_workload_mid_bf16_4k(gpu_lib):
+    _workload_check(gpu_lib, "mid_bf16_4k", rows_cap=512)
+
+
+def test_workload_long_bf16_32k_sampled(gpu_lib):
+    _workload_check(gpu_lib, "long_bf16_32k", rows_cap=48)
+
+
+@pytest.mark.parametrize("k", [512, 1024, 2048])
+def test_workload_vlong_bf16_100k_sampled(gpu_lib, k):
+    import torch
+    w = WORKLOADS["vlong_bf16_100k"]
+    x = generate(w)
+    rows = sample_rows(w)[::8]
+    res = _run_oracle_prefill(gpu_lib, x, "bf16", k)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    check_support_rows(res["idx"], res["count"], layer, rows, k)
+    check_outputs_on_gpu_support(res["out"], None, layer, rows, res["idx"], res["count"], 1,
+                                 "bf16")
+
+
+# ----------------------------------------------------------------- indexer
+def _indexer_run(amtk, qi, ki, k, key_block):
+    import torch
+    idx, cnt, mass = amtk.indexer_topk(torch.from_numpy(qi).to(torch.bfloat16).cuda(),
+                                       torch.from_numpy(ki).to(torch.bfloat16).cuda(), k,
+                                       key_block)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy(), mass.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k,kb", [(1000, 4, 64), (300, 16, 1), (64, 2, 64), (65, 1, 64)])
+def test_indexer_small(gpu_lib, n, k, kb):
+    rng = np.random.default_rng(n + k)
+    from synth import round_bf16
+    qi = round_bf16(rng.standard_normal((n, 64)).astype(np.float32))
+    ki = round_bf16(rng.standard_normal((n, 64)).astype(np.float32))
+    idx, cnt, mass = _indexer_run(gpu_lib, qi, ki, k, kb)
+    ix = IndexerOracle(qi, ki)
+    for i in range(n):
+        r = ix.row(i, k, kb)
+        from tests.support_rules import check_row
+        ok, msg, _ = check_row(idx[i], cnt[i], r["score"], r["kth"], k, BAND)
+        assert ok, f"row {i}: {msg}"
+        sel = idx[i][: cnt[i]]
+        assert np.all(np.abs(mass[i][: cnt[i]] - r["score"][sel]) <= 1e-7 + 2e-4 * r["score"][sel])
+
+
+def test_indexer_zero_queries_tie_by_block_size(gpu_lib):
+    n = 500
+    qi = np.zeros((n, 64), dtype=np.float32)
+    ki = np.random.default_rng(1).standard_normal((n, 64)).astype(np.float32)
+    from synth import round_bf16
+    idx, cnt, _ = _indexer_run(gpu_lib, qi, round_bf16(ki), 2, 64)
+    for i in range(n):
+        nb = i // 64 + 1
+        if nb <= 2:
+            assert idx[i][: cnt[i]].tolist() == list(range(nb))
+        elif (i + 1) % 64 == 0:
+            assert idx[i][:2].tolist() == [0, 1]          # all blocks full: smallest ids
+        else:
+            assert idx[i][:2].tolist() == [0, 1]          # full blocks outweigh the partial one
+
+
+def test_workload_indexer_bf16_32k_sampled(gpu_lib):
+    import torch
+    amtk = gpu_lib
+    w = WORKLOADS["indexer_bf16_32k"]
+    x = generate(w)
+    rows = sample_rows(w)[::4]
+    idx, cnt, _ = _indexer_run(amtk, x["q_idx"], x["k_idx"], w.k, w.key_block)
+    ix = IndexerOracle(x["q_idx"], x["k_idx"])
+    check_support_rows(idx, cnt, None, rows, w.k,
+                       scores=lambda i: (lambda r: (r["score"], r["kth"]))(ix.row(int(i), w.k, 64)))
+    d = upload(x, "bf16")
+    out, _ = amtk.sparse_attn(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
+                              torch.from_numpy(cnt).cuda(), 64)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    check_outputs_on_gpu_support(out.cpu().numpy(), None, layer, rows, idx, cnt, 64, "bf16")
