@@ -126,7 +126,21 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="budget (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run one plain device copy of MB megabytes (to scale HBM "
+                         "traffic counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        nbytes = args.calibrate_copy * 1000 * 1000
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": nbytes,
+                          "bytes_written": nbytes}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "path shards by query rows across GPUs, which is not built here.", file=sys.stderr)

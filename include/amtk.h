@@ -62,8 +62,9 @@ typedef struct {
   int32_t key_block;     /* 1 = token support, 64 = aligned 64-token key blocks */
   int32_t query_block;   /* queries sharing one support (b_sel); must be 1 */
   int32_t candidate_cap; /* candidates kept per row by the streaming filter;
-                            0 = automatic. Rows that exceed it are recomputed
-                            densely, so any value >= 1 gives the same result. */
+                            0 = automatic; values above 65000 are clamped.
+                            Rows that exceed it are recomputed densely, so
+                            any value >= 1 gives the same result. */
 } amtk_support_desc;
 
 /* Bytes of device workspace topk_support / oracle_prefill need for these

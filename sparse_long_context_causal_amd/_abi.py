@@ -2,7 +2,10 @@
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libamtk.so")
+# AMTK_LIBRARY may point at another build of the same library (e.g. a variant
+# compiled with different flags); by default the in-tree libamtk.so is used.
+LIB_PATH = os.environ.get("AMTK_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libamtk.so")
 
 AMTK_OK = 0
 AMTK_E_INVALID = -1

@@ -20,6 +20,10 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
+// Candidate pool capacity per row is kept below 2^16 - 32: the pass-2 filter
+// counts candidates per mass bin in 16-bit LDS counters.
+constexpr int kMaxCap = 65000;
+
 int hip_fail(hipError_t e) {
   g_last_hip = (int)e;
   return AMTK_E_HIP;
@@ -68,6 +72,7 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
   int cap = sp.candidate_cap > 0 ? sp.candidate_cap
                                  : (8 * sp.k > 4096 ? 8 * sp.k : 4096);
   if (cap > L.units_max) cap = L.units_max;
+  if (cap > kMaxCap) cap = kMaxCap;
   L.cap = cap;
   size_t off = 0;
   L.cand = off;       off = round_up(off + n * (size_t)cap * sizeof(uint2));

@@ -75,6 +75,84 @@ struct Mma<float> {
   }
 };
 
+// ------------------------------------------------------ K tiles through LDS
+// A wave stages a 32-row key tile for one KV head in its own LDS slot with
+// direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land
+// at slot + 16*l), so the prefetch holds no VGPRs. Each lane loads the half
+// row its MFMA A operand needs (row l%32, d half l/32) as kChunks 16-byte
+// chunks; chunk c of every lane forms the 1 KiB block slot + 1024*c.
+template <typename T, int D>
+struct KTile {
+  static constexpr int kChunks = (D / 2) * (int)sizeof(T) / 16;   // 16 B chunks per lane
+  static constexpr int kBytes = kChunks * 1024;                   // LDS bytes per slot
+};
+
+// MFMA over one 16-byte chunk per lane of A and B: one 32x32x16 bf16 step,
+// or four 32x32x2 fp32 steps.
+template <typename T>
+struct ChunkMma;
+
+template <>
+struct ChunkMma<bf16_t> {
+  static constexpr int kSteps = 1;   // MFMA instructions per chunk
+  __device__ __forceinline__ static void mma(f32x16& acc, uint4 a, uint4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct ChunkMma<float> {
+  static constexpr int kSteps = 4;
+  __device__ __forceinline__ static void mma(f32x16& acc, uint4 a, uint4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void dma_chunk(const void* gsrc, void* lds_slot_chunk) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)lds_slot_chunk, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// Reads 4 consecutive 1 KiB chunks (this lane's 16 bytes of each) and waits
+// for them inside the same asm block.
+__device__ __forceinline__ void lds_read4(uint32_t addr, uint4& a, uint4& b, uint4& c, uint4& d) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(a), "=v"(b), "=v"(c), "=v"(d)
+      : "v"(addr)
+      : "memory");
+}
+
+// Scheduling hint for a software-pipelined tile: the first `lead` MFMAs
+// alone, then one MFMA per `valu` VALU instructions for `pairs` rounds, then
+// the remaining VALU work. Masks: 0x008 = MFMA, 0x002 = VALU.
+template <int lead, int pairs, int valu>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#ifndef AMTK_NO_SCHED_HINTS
+  __builtin_amdgcn_sched_group_barrier(0x008, lead, 0);
+#pragma unroll
+  for (int i = 0; i < pairs; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, valu, 0);
+  }
+#endif
+}
+
 // Row of key / query m inside a 32-row tile held by accumulator register r.
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 

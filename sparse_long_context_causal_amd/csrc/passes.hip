@@ -8,15 +8,23 @@
 // averages the heads into one token-importance distribution and keeps its
 // top-k units as the support. The abstract states the same oracle.
 //
-// Work decomposition (one workgroup = 32 consecutive query rows):
-//   * wave g owns KV head g and the G query heads that read it; its G query
-//     tiles stay in VGPRs for the whole launch (MFMA B operands);
-//   * key tiles of 32 rows stream from HBM/L2 straight into VGPRs (MFMA A
-//     operands), one tile ahead of the math;
+// Work decomposition (one workgroup = 32 consecutive query rows, one wave
+// per KV head g):
+//   * wave g keeps the 32 x d query tiles of its G heads in VGPRs for the
+//     whole launch (MFMA B operands, 16-byte chunks per lane);
+//   * 32-row key tiles of KV head g stream through the wave's own LDS slot
+//     by direct global->LDS loads issued one tile ahead (no VGPRs held), and
+//     are read back as MFMA A operands;
+//   * the G heads are software pipelined inside the wave: the MFMAs of head
+//     h+1 are issued before the exp/sum work of head h, so the matrix core
+//     and the VALU run side by side;
+//   * the diagonal tile (causal mask) is peeled out of the main loop;
 //   * pass 1 keeps an online max / sum per (head, query) in registers;
 //   * pass 2 turns logits into probabilities with pass 1's LSE, sums the G
-//     heads of the wave in registers, sums the Hkv waves through LDS in a
-//     fixed order, and filters the averaged mass against a per-row bound.
+//     heads in registers, and the Hkv partial sums meet in LDS (double
+//     buffered, one barrier per key tile). Each wave then owns 32/Hkv query
+//     rows: it reduces their masses over the KV heads in a fixed order and
+//     filters them against the row's bound, so row state needs no atomics.
 // Workgroups are issued longest-row first (causal load balance).
 //
 // Streaming filter (pass 2). Per query row, an LDS histogram over mass bins
@@ -32,6 +40,64 @@
 
 namespace amtk {
 
+// Mass bins for the filter: 8 per octave from 2^-48 to 2^1, u16 counts
+// packed two per LDS word. Masses below 2^-48 share bin 0.
+constexpr int kFBinBase = (127 - 48) << 3;
+constexpr int kFBins = 49 * 8;
+constexpr int kFBinWords = kFBins / 2;
+
+__device__ __forceinline__ int filter_bin(float p) {
+  const int b = (int)(__float_as_uint(p) >> kBinShift) - kFBinBase;
+  return min(max(b, 0), kFBins - 1);
+}
+
+__device__ __forceinline__ int hist_count(const unsigned* words, int b) {
+  return (int)((words[b >> 1] >> ((b & 1) * 16)) & 0xffffu);
+}
+
+// ---------------------------------------------------------------- K tiles
+template <typename T, int D>
+__device__ __forceinline__ void issue_k_tile(const T* __restrict__ K, int n, int hkv, int g,
+                                             int k0, int lane, unsigned char* slot) {
+  typedef KTile<T, D> KT;
+  const int row = min(k0 + (lane & 31), n - 1);
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(
+      K + ((size_t)row * hkv + g) * D + (lane >> 5) * (D / 2));
+#pragma unroll
+  for (int c = 0; c < KT::kChunks; ++c) dma_chunk(src + 16 * c, slot + 1024 * c);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void read_k_tile(const unsigned char* slot, int lane,
+                                            uint4 (&kc)[KTile<T, D>::kChunks]) {
+  typedef KTile<T, D> KT;
+  const uint32_t a = lds_addr(slot) + 16 * lane;
+#pragma unroll
+  for (int c = 0; c < KT::kChunks; c += 4)
+    lds_read4(a + 1024 * c, kc[c], kc[c + 1], kc[c + 2], kc[c + 3]);
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_q_tiles(const T* __restrict__ Q, int qrow, int hq, int g,
+                                             int lane, uint4 (&qc)[G][KTile<T, D>::kChunks]) {
+  typedef KTile<T, D> KT;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4* src = reinterpret_cast<const uint4*>(Q + ((size_t)qrow * hq + g * G + h) * D +
+                                                      (lane >> 5) * (D / 2));
+#pragma unroll
+    for (int c = 0; c < KT::kChunks; ++c) qc[h][c] = src[c];
+  }
+}
+
+template <typename T, int NC>
+__device__ __forceinline__ void score_tile(f32x16& acc, const uint4 (&kc)[NC],
+                                           const uint4 (&qc)[NC]) {
+  acc = f32x16{};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ChunkMma<T>::mma(acc, kc[c], qc[c]);
+}
+
 // ------------------------------------------------------------------ pass 1
 template <typename T, int D, int G>
 __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
@@ -39,8 +105,9 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
                                                          float* __restrict__ lse, int n, int hkv,
                                                          float c, float tau,
                                                          int* __restrict__ zero_counter) {
-  typedef Mma<T> M;
-  constexpr int STEPS = D / M::kPerStep;
+  typedef KTile<T, D> KT;
+  constexpr int NC = KT::kChunks;
+  extern __shared__ __align__(16) unsigned char smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
   const int g = wave;
@@ -48,16 +115,12 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   const int ntiles = (n + 31) >> 5;
   const int qt = ntiles - 1 - (int)blockIdx.x;
   const int q0 = qt << 5;
+  unsigned char* slot = smem + wave * KT::kBytes;
   if (blockIdx.x == 0 && threadIdx.x == 0 && zero_counter) *zero_counter = 0;
 
-  const int qrow = min(q0 + col, n - 1);
-  typename M::frag qf[G][STEPS];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const T* qp = Q + ((size_t)qrow * hq + g * G + h) * D + hf * (D / 2);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) qf[h][s] = M::load(qp, s);
-  }
+  issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot);
+  uint4 qc[G][NC];
+  load_q_tiles<T, D, G>(Q, min(q0 + col, n - 1), hq, g, lane, qc);
   float mrun[G], lrun[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -65,48 +128,44 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
     lrun[h] = 0.f;
   }
 
-  typename M::frag kf[STEPS];
-  {
-    const int kr = min(col, n - 1);
-    const T* kp = K + ((size_t)kr * hkv + g) * D + hf * (D / 2);
+  // exp/sum work of one head on its score tile (16 keys x 1 query per lane)
+  auto stats = [&](f32x16& acc, int h, bool diag) {
+    if (diag) {
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) kf[s] = M::load(kp, s);
-  }
-  for (int kt = 0; kt <= qt; ++kt) {
-    typename M::frag kn[STEPS];
-    if (kt < qt) {
-      const int kr = min(((kt + 1) << 5) + col, n - 1);
-      const T* kp = K + ((size_t)kr * hkv + g) * D + hf * (D / 2);
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) kn[s] = M::load(kp, s);
+      for (int r = 0; r < 16; ++r)
+        if (acc_row(r, hf) > col) acc[r] = -INFINITY;
     }
-    const bool diag = (kt == qt);
+    float tmax = fmaxf(acc[0], acc[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+    const float mnew = fmaxf(mrun[h], tmax);
+    const float mc = mnew * c;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      s0 += fast_exp2(fmaf(acc[r], c, -mc));
+      s1 += fast_exp2(fmaf(acc[r + 1], c, -mc));
+    }
+    lrun[h] = fmaf(lrun[h], fast_exp2((mrun[h] - mnew) * c), s0 + s1);
+    mrun[h] = mnew;
+  };
+  auto tile = [&](int kt, bool diag) {
+    uint4 kc[NC];
+    wait_vmem_all();
+    read_k_tile<T, D>(slot, lane, kc);
+    if (kt < qt) issue_k_tile<T, D>(K, n, hkv, g, (kt + 1) << 5, lane, slot);
+    f32x16 a0, a1;
+    score_tile<T, NC>(a0, kc, qc[0]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) M::mma(acc, kf[s], qf[h][s]);
-      if (diag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_row(r, hf) > col) acc[r] = -INFINITY;
-      }
-      float tmax = acc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
-      const float mnew = fmaxf(mrun[h], tmax);
-      const float mc = mnew * c;
-      float sum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[r], c, -mc));
-      lrun[h] = lrun[h] * fast_exp2((mrun[h] - mnew) * c) + sum;
-      mrun[h] = mnew;
+      if (h + 1 < G) score_tile<T, NC>((h & 1) ? a0 : a1, kc, qc[h + 1]);
+      stats((h & 1) ? a1 : a0, h, diag);
     }
-    if (kt < qt) {
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) kf[s] = kn[s];
-    }
-  }
+    if (!diag) interleave_mfma_valu<NC * ChunkMma<T>::kSteps, (G - 1) * NC * ChunkMma<T>::kSteps, 64 / (NC * ChunkMma<T>::kSteps)>();
+  };
+  for (int kt = 0; kt < qt; ++kt) tile(kt, false);
+  tile(qt, true);
+
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float mo = xor32f(mrun[h]), lo = xor32f(lrun[h]);
@@ -125,17 +184,27 @@ struct RowState {
 };
 
 // Raise the row's bound while more than k candidates lie strictly above it.
-__device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* hist, int r, int budget) {
+__device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* words, int r,
+                                            int budget) {
   const int fresh = rs.cnt[r] - rs.seen[r];
   rs.seen[r] = rs.cnt[r];
   int cg = rs.cge[r] + fresh;
   int bt = rs.btau[r];
-  while (bt < kNumBins - 1 && cg - (int)hist[bt] >= budget) {
-    cg -= (int)hist[bt];
+  while (bt < kFBins - 1) {
+    const int hb = hist_count(words, bt);
+    if (cg - hb < budget) break;
+    cg -= hb;
     ++bt;
   }
   rs.cge[r] = cg;
   rs.btau[r] = bt;
+}
+
+// Swizzled partial-mass layout: element (register r, source lane) of KV head
+// g's tile lives at word r*64 + ((lane + 4r) & 63) of that head's 4 KiB block,
+// so both the lane-major writes and the row-owner reads are bank-conflict free.
+__device__ __forceinline__ int part_index(int g, int r, int src_lane) {
+  return (g * 16 + r) * 64 + ((src_lane + 4 * r) & 63);
 }
 
 template <typename T, int D, int G, int KB>
@@ -144,12 +213,14 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     int hkv, float c, float inv_hq, int budget, uint2* __restrict__ cand, int cap,
     int* __restrict__ cand_count, int* __restrict__ row_bin, int* __restrict__ ovf_count,
     int* __restrict__ ovf_list) {
-  typedef Mma<T> M;
-  constexpr int STEPS = D / M::kPerStep;
+  typedef KTile<T, D> KT;
+  constexpr int NC = KT::kChunks;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned* hist = reinterpret_cast<unsigned*>(smem);                      // [32][kNumBins]
-  RowState& rs = *reinterpret_cast<RowState*>(hist + 32 * kNumBins);
+  unsigned* hist = reinterpret_cast<unsigned*>(smem);                       // [32][kFBinWords]
+  RowState& rs = *reinterpret_cast<RowState*>(hist + 32 * kFBinWords);
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(&rs) + sizeof(RowState));
+  const int part_floats = (KB == 1) ? hkv * 16 * 64 : hkv * 32;           // one buffer
+  unsigned char* slots = reinterpret_cast<unsigned char*>(part + 2 * part_floats);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
@@ -159,103 +230,98 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   const int ntiles = (n + 31) >> 5;
   const int qt = ntiles - 1 - (int)blockIdx.x;
   const int q0 = qt << 5;
-  const int q = q0 + col;
-  const int qrow = min(q, n - 1);
+  const int qrow = min(q0 + col, n - 1);
+  unsigned char* slot = slots + wave * KT::kBytes;
 
-  for (int t = threadIdx.x; t < 32 * kNumBins; t += nthreads) hist[t] = 0u;
+  issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot);
+  for (int t = threadIdx.x; t < 32 * kFBinWords; t += nthreads) hist[t] = 0u;
   if (threadIdx.x < 32) {
     rs.cnt[threadIdx.x] = 0;
     rs.seen[threadIdx.x] = 0;
     rs.cge[threadIdx.x] = 0;
     rs.btau[threadIdx.x] = 0;
   }
-
-  typename M::frag qf[G][STEPS];
+  uint4 qc[G][NC];
+  load_q_tiles<T, D, G>(Q, qrow, hq, g, lane, qc);
   float bias[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const T* qp = Q + ((size_t)qrow * hq + g * G + h) * D + hf * (D / 2);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) qf[h][s] = M::load(qp, s);
-    bias[h] = lse[(size_t)(g * G + h) * n + qrow] * kLog2e;
-  }
-  typename M::frag kf[STEPS];
-  {
-    const int kr = min(col, n - 1);
-    const T* kp = K + ((size_t)kr * hkv + g) * D + hf * (D / 2);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) kf[s] = M::load(kp, s);
-  }
+  for (int h = 0; h < G; ++h) bias[h] = lse[(size_t)(g * G + h) * n + qrow] * kLog2e;
+
+  // Row ownership: wave w owns query rows [w*qpw, (w+1)*qpw) of the tile;
+  // lpq lanes serve one row, each with epl of its 32 keys.
+  const int qpw = 32 / hkv, lpq = 2 * hkv, epl = 16 / hkv;
+  const int own_n = wave * qpw + lane / lpq;       // tile-local row this lane serves
+  const int own_j = lane % lpq;
+  const int own_q = q0 + own_n;
+  const unsigned long long grp_mask =
+      (lpq == 64 ? ~0ull : ((1ull << lpq) - 1ull)) << ((lane / lpq) * lpq);
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  unsigned* own_hist = hist + own_n * kFBinWords;
   __syncthreads();
 
-  float blk = 0.f;   // KB > 1: this query's mass over the current key block (this wave's heads)
-  for (int kt = 0; kt <= qt; ++kt) {
-    const int k0 = kt << 5;
-    typename M::frag kn[STEPS];
-    if (kt < qt) {
-      const int kr = min(k0 + 32 + col, n - 1);
-      const T* kp = K + ((size_t)kr * hkv + g) * D + hf * (D / 2);
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) kn[s] = M::load(kp, s);
-    }
-    const bool diag = (kt == qt);
-    float pacc[16];
+  // head-summed probabilities of one key tile for this lane's query
+  auto tile_mass = [&](int kt, bool diag, float (&pacc)[16]) {
+    uint4 kc[NC];
+    wait_vmem_all();
+    read_k_tile<T, D>(slot, lane, kc);
+    if (kt < qt) issue_k_tile<T, D>(K, n, hkv, g, (kt + 1) << 5, lane, slot);
 #pragma unroll
     for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+    f32x16 a0, a1;
+    score_tile<T, NC>(a0, kc, qc[0]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      f32x16 acc = {};
+      if (h + 1 < G) score_tile<T, NC>((h & 1) ? a0 : a1, kc, qc[h + 1]);
+      const f32x16& a = (h & 1) ? a1 : a0;
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) M::mma(acc, kf[s], qf[h][s]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pacc[r] += fast_exp2(fmaf(acc[r], c, -bias[h]));
+      for (int r = 0; r < 16; ++r) pacc[r] += fast_exp2(fmaf(a[r], c, -bias[h]));
     }
+    if (!diag) interleave_mfma_valu<NC * ChunkMma<T>::kSteps, (G - 1) * NC * ChunkMma<T>::kSteps, 48 / (NC * ChunkMma<T>::kSteps)>();
     if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (acc_row(r, hf) > col) pacc[r] = 0.f;
     }
+  };
+
+  float blk = 0.f;   // KB > 1: this query's mass over the current key block (this wave's heads)
+  for (int kt = 0; kt <= qt; ++kt) {
+    const int k0 = kt << 5;
+    const bool diag = kt == qt;
+    float pacc[16];
+    if (diag) tile_mass(kt, true, pacc);
+    else tile_mass(kt, false, pacc);
 
     if constexpr (KB == 1) {
-      // ---- token units: sum the Hkv partial masses, filter, append
+      float* pb = part + (kt & 1) * part_floats;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part[(g * 16 + r) * 64 + lane] = pacc[r];
+      for (int r = 0; r < 16; ++r) pb[part_index(g, r, lane)] = pacc[r];
       __syncthreads();
-      const int rpw = 16 / hkv;          // accumulator rows reduced by this wave
-      const int bt = rs.btau[col];
-      // element rr of this lane: its averaged mass, key id and filter verdict
-      auto elem = [&](int rr, float& p, int& key) -> bool {
-        const int r = wave * rpw + rr;
-        p = 0.f;
-        for (int gg = 0; gg < hkv; ++gg) p += part[(gg * 16 + r) * 64 + lane];
+      // ---- row owner: reduce over KV heads, filter, append, raise the bound
+      const int bt = rs.btau[own_n];
+      const bool live = own_q < n && rs.cnt[own_n] <= cap;
+      int pos = rs.cnt[own_n];
+      for (int e = 0; e < epl; ++e) {
+        const int f = e * lpq + own_j;
+        const int r = f & 15, h2 = f >> 4;
+        float p = 0.f;
+        for (int gg = 0; gg < hkv; ++gg) p += pb[part_index(gg, r, own_n + 32 * h2)];
         p *= inv_hq;
-        key = k0 + acc_row(r, hf);
-        return (q < n) && (key <= q) && (mass_bin(p) >= bt);
-      };
-      int kept = 0;
-      for (int rr = 0; rr < rpw; ++rr) {
-        float p;
-        int key;
-        kept += elem(rr, p, key) ? 1 : 0;
-      }
-      const int other = xor32i(kept);
-      int base = 0;
-      if (hf == 0 && kept + other > 0) base = atomicAdd(&rs.cnt[col], kept + other);
-      base = __shfl(base, col, 64);
-      int pos = hf ? base + other : base;
-      uint2* row = cand + (size_t)qrow * cap;
-      unsigned* rh = hist + col * kNumBins;
-      for (int rr = 0; rr < rpw; ++rr) {
-        float p;
-        int key;
-        if (elem(rr, p, key)) {
-          if (pos < cap) row[pos] = make_uint2(__float_as_uint(p), (unsigned)key);
-          atomicAdd(&rh[mass_bin(p)], 1u);
-          ++pos;
+        const int key = k0 + acc_row(r, h2);
+        const int bin = filter_bin(p);
+        const bool flag = own_q < n && key <= own_q && bin >= bt;
+        const unsigned long long m = __ballot(flag) & grp_mask;
+        if (flag) {
+          const int at = pos + __popcll(m & below);
+          if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(__float_as_uint(p), (unsigned)key);
+          if (live) atomicAdd(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
         }
+        pos += __popcll(m);
       }
-      __syncthreads();
-      if (threadIdx.x < 32) raise_bound(rs, hist + threadIdx.x * kNumBins, threadIdx.x, budget);
+      if (own_j == 0 && own_q < n) {
+        rs.cnt[own_n] = pos;
+        if (pos <= cap) raise_bound(rs, own_hist, own_n, budget);
+      }
     } else {
       // ---- key blocks of KB = 64 tokens = two key tiles
       float ps = 0.f;
@@ -263,31 +329,28 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       for (int r = 0; r < 16; ++r) ps += pacc[r];
       ps += xor32f(ps);
       blk += ps;
-      const bool blk_end = (kt & 1) || diag;
-      if (blk_end) {
+      if ((kt & 1) || diag) {
         const int b = kt >> 1;
-        float* pb = part + (b & 1) * hkv * 32;
+        float* pb = part + (b & 1) * part_floats;
         if (hf == 0) pb[g * 32 + col] = blk;
         blk = 0.f;
         __syncthreads();
-        if (threadIdx.x < 32) {
-          const int r = threadIdx.x;
-          const int qq = q0 + r;
+        if (own_j == 0 && own_q < n) {
           float p = 0.f;
-          for (int gg = 0; gg < hkv; ++gg) p += pb[gg * 32 + r];
+          for (int gg = 0; gg < hkv; ++gg) p += pb[gg * 32 + own_n];
           p *= inv_hq;
-          if (qq < n && b * KB <= qq && mass_bin(p) >= rs.btau[r]) {
-            const int pos = rs.cnt[r]++;
-            if (pos < cap) cand[(size_t)qq * cap + pos] = make_uint2(__float_as_uint(p), (unsigned)b);
-            hist[r * kNumBins + mass_bin(p)] += 1u;
-            raise_bound(rs, hist + r * kNumBins, r, budget);
+          const int bin = filter_bin(p);
+          if (bin >= rs.btau[own_n]) {
+            const int at = rs.cnt[own_n];
+            if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(__float_as_uint(p), (unsigned)b);
+            rs.cnt[own_n] = at + 1;
+            if (at + 1 <= cap) {
+              own_hist[bin >> 1] += 1u << ((bin & 1) * 16);
+              raise_bound(rs, own_hist, own_n, budget);
+            }
           }
         }
       }
-    }
-    if (kt < qt) {
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) kf[s] = kn[s];
     }
   }
   __syncthreads();
@@ -308,15 +371,22 @@ static hipError_t run_pass1(const LayerShape& s, const void* q, const void* k, f
                             int* zero_counter, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
   const float tau = s.scale;
-  hipLaunchKernelGGL((pass1_lse_kernel<T, D, G>), dim3(ntiles), dim3(64 * s.hkv), 0, stream,
+  const size_t lds = (size_t)s.hkv * KTile<T, D>::kBytes;
+  auto kern = pass1_lse_kernel<T, D, G>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
                      tau * kLog2e, tau, zero_counter);
   return hipGetLastError();
 }
 
+template <typename T, int D>
 static size_t pass2_lds_bytes(int hkv, int key_block) {
-  size_t b = 32 * kNumBins * sizeof(unsigned) + sizeof(RowState);
-  b += (key_block == 1) ? (size_t)hkv * 16 * 64 * sizeof(float) : (size_t)2 * hkv * 32 * sizeof(float);
+  size_t b = 32 * kFBinWords * sizeof(unsigned) + sizeof(RowState);
+  b += 2 * ((key_block == 1) ? (size_t)hkv * 16 * 64 : (size_t)hkv * 32) * sizeof(float);
+  b += (size_t)hkv * KTile<T, D>::kBytes;
   return b;
 }
 
@@ -324,7 +394,7 @@ template <typename T, int D, int G, int KB>
 static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, const void* k,
                             const float* lse, const CandidatePool& pool, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
-  const size_t lds = pass2_lds_bytes(s.hkv, KB);
+  const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB);
   auto kern = pass2_filter_kernel<T, D, G, KB>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
