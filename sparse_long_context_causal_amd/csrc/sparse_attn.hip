@@ -180,6 +180,182 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for bf16, d = 128, 8 KV heads x 4 query heads each (the shape of
+// the long-context GQA layers). One wave per query row; lane l serves KV head
+// g = l/8 and the 16 elements d in [16*(l%8), 16*(l%8)+16) of the K/V rows.
+//  * QK: v_dot2 on raw bf16 pairs (no conversion), 8 per head and token.
+//  * The 8 lanes of a KV head finish its 4 logits with a transposed DPP
+//    butterfly (half-mirror, xor1, xor2): afterwards lane l holds the full
+//    logit of head h(l) = 2*((l>>2)&1) + (l&1) of its group (lanes l and l^2
+//    share a head). The online softmax then costs one exp per lane and token.
+//  * The 4 heads' weights are gathered back into every lane with DPP for the
+//    fp32 P*V update (P is never rounded).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppBcast0 = 0x00;      // quad_perm [0,0,0,0]
+constexpr int kDppBcast1 = 0x55;      // quad_perm [1,1,1,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Values of x held by the lanes of heads 0..3 of this lane's group.
+__device__ __forceinline__ void gather4(float x, bool b2, float (&out)[4]) {
+  const float qa = dpp<kDppBcast0>(x), qb = dpp<kDppBcast1>(x);
+  const float ma = dpp<kDppHalfMirror>(qa), mb = dpp<kDppHalfMirror>(qb);
+  out[0] = b2 ? ma : qa;
+  out[1] = b2 ? mb : qb;
+  out[2] = b2 ? qa : ma;
+  out[3] = b2 ? qb : mb;
+}
+
+template <int CH>
+__global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
+    float* __restrict__ lse_out, int n, int key_block, int max_units, float c) {
+  constexpr int D = 128, HKV = 8, G = 4, E = 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = n - 1 - (int)(blockIdx.x * kAttnWaves + wave);
+  if (i < 0) return;
+  const int g = lane >> 3, sub = lane & 7;
+  const bool b2 = (sub >> 2) & 1, b0 = sub & 1;
+  const int myh = 2 * (int)b2 + (int)b0;
+  const int e0 = sub * E;
+  const size_t off = (size_t)g * D + e0;
+
+  unsigned qd[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4* qp = reinterpret_cast<const uint4*>(Q + ((size_t)i * (HKV * G) + g * G + h) * D + e0);
+    const uint4 a = qp[0], b = qp[1];
+    qd[h][0] = a.x; qd[h][1] = a.y; qd[h][2] = a.z; qd[h][3] = a.w;
+    qd[h][4] = b.x; qd[h][5] = b.y; qd[h][6] = b.z; qd[h][7] = b.w;
+  }
+  float acc[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  float m = kNegBig, l = 0.f;   // softmax state of head myh
+
+  const int cnt = min(max(count[i], 0), max_units);
+  const int total = cnt * key_block;
+  const int32_t* ids = idx + (size_t)i * max_units;
+
+  for (int t0 = 0; t0 < total; t0 += CH) {
+    int jj[CH];
+    bool ok[CH];
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const int tt = t0 + cc;
+      bool v = tt < total;
+      const int u = key_block == 1 ? tt : tt / key_block;
+      const int base = v ? ids[u] : 0;
+      const int j = key_block == 1 ? base : base * key_block + (tt - u * key_block);
+      v = v && base >= 0 && j <= i;
+      ok[cc] = v;
+      jj[cc] = v ? j : i;
+    }
+    uint4 kx[CH][2], vx[CH][2];
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const uint4* kp = reinterpret_cast<const uint4*>(K + (size_t)jj[cc] * (HKV * D) + off);
+      const uint4* vp = reinterpret_cast<const uint4*>(V + (size_t)jj[cc] * (HKV * D) + off);
+      kx[cc][0] = kp[0];
+      kx[cc][1] = kp[1];
+      vx[cc][0] = vp[0];
+      vx[cc][1] = vp[1];
+    }
+    // logits of head myh for the chunk's tokens, in log2 units
+    float x[CH];
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const unsigned kd[8] = {kx[cc][0].x, kx[cc][0].y, kx[cc][0].z, kx[cc][0].w,
+                              kx[cc][1].x, kx[cc][1].y, kx[cc][1].z, kx[cc][1].w};
+      float s[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; w += 2) {
+          a0 = dot2(qd[h][w], kd[w], a0);
+          a1 = dot2(qd[h][w + 1], kd[w + 1], a1);
+        }
+        s[h] = a0 + a1;
+      }
+      const float k0 = b2 ? s[2] : s[0], k1 = b2 ? s[3] : s[1];
+      const float t0v = k0 + dpp<kDppHalfMirror>(b2 ? s[0] : s[2]);
+      const float t1v = k1 + dpp<kDppHalfMirror>(b2 ? s[1] : s[3]);
+      const float u = (b0 ? t1v : t0v) + dpp<kDppXor1>(b0 ? t0v : t1v);
+      const float tot = u + dpp<kDppXor2>(u);
+      x[cc] = ok[cc] ? __fmul_rn(tot, c) : -INFINITY;
+    }
+    float cmax = kNegBig;
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) cmax = fmaxf(cmax, x[cc]);
+    const float mnew = fmaxf(m, cmax);
+    const float alpha = m == mnew ? 1.0f : fast_exp2(m - mnew);
+    float p[CH];
+    float ps = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      // the running maximum weighs exactly 1 (exp2 of 0 is only ~1 ulp exact)
+      p[cc] = x[cc] == mnew ? 1.0f : fast_exp2(x[cc] - mnew);
+      ps += p[cc];
+    }
+    l = fmaf(l, alpha, ps);
+    m = mnew;
+    float a4[4];
+    gather4(alpha, b2, a4);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= a4[h];
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      float p4[4];
+      gather4(p[cc], b2, p4);
+      const unsigned vd[8] = {vx[cc][0].x, vx[cc][0].y, vx[cc][0].z, vx[cc][0].w,
+                              vx[cc][1].x, vx[cc][1].y, vx[cc][1].z, vx[cc][1].w};
+      float vf[E];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        vf[2 * w] = __uint_as_float(vd[w] << 16);
+        vf[2 * w + 1] = __uint_as_float(vd[w] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p4[h], vf[e], acc[h][e]);
+    }
+  }
+  float l4[4], m4[4];
+  gather4(l, b2, l4);
+  gather4(m, b2, m4);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float inv = l4[h] > 0.f ? 1.0f / l4[h] : 0.f;
+    float4* op = reinterpret_cast<float4*>(O + ((size_t)i * (HKV * G) + g * G + h) * D + e0);
+#pragma unroll
+    for (int v4 = 0; v4 < E / 4; ++v4)
+      op[v4] = make_float4(acc[h][4 * v4] * inv, acc[h][4 * v4 + 1] * inv,
+                           acc[h][4 * v4 + 2] * inv, acc[h][4 * v4 + 3] * inv);
+  }
+  if (lse_out && (sub == 0 || sub == 1 || sub == 4 || sub == 5))
+    lse_out[(size_t)(g * G + myh) * n + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
 template <typename T, int E, int G>
 static hipError_t run_attn(const LayerShape& s, int key_block, int max_units, const void* q,
                            const void* k, const void* v, const int32_t* idx,
@@ -239,6 +415,15 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
                               const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream) {
+  if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32) {
+    constexpr int CH = 4;
+    const int blocks = (s.n + kAttnWaves - 1) / kAttnWaves;
+    hipLaunchKernelGGL((sparse_attn_g4_kernel<CH>), dim3(blocks), dim3(64 * kAttnWaves), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, key_block,
+                       max_units, s.scale * kLog2e);
+    return hipGetLastError();
+  }
   if (s.dtype == kBF16)
     return attn_by_e<bf16_t>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
   return attn_by_e<float>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
