@@ -120,12 +120,21 @@ __device__ __forceinline__ void dma_chunk(const void* gsrc, void* lds_slot_chunk
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Waits until at most N vector-memory operations of this wave are in flight
+// (vector memory operations retire in issue order for this count).
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
 
 // Reads 4 consecutive 1 KiB chunks (this lane's 16 bytes of each) and waits
-// for them inside the same asm block.
+// for them inside the same asm block. The outputs are early-clobber ("=&v"):
+// a load that lands while later loads of the block are still being issued
+// must not overwrite the address register they use.
 __device__ __forceinline__ void lds_read4(uint32_t addr, uint4& a, uint4& b, uint4& c, uint4& d) {
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
@@ -133,7 +142,7 @@ __device__ __forceinline__ void lds_read4(uint32_t addr, uint4& a, uint4& b, uin
       "ds_read_b128 %2, %4 offset:2048\n\t"
       "ds_read_b128 %3, %4 offset:3072\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(a), "=v"(b), "=v"(c), "=v"(d)
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
       : "v"(addr)
       : "memory");
 }
@@ -151,6 +160,22 @@ __device__ __forceinline__ void interleave_mfma_valu() {
     __builtin_amdgcn_sched_group_barrier(0x002, valu, 0);
   }
 #endif
+}
+
+// Workgroup barriers that do not drain vector memory: __syncthreads() makes
+// the compiler wait for every outstanding load (vmcnt(0)), which would stall
+// the per-wave global->LDS key prefetch at each barrier. barrier_lds() waits
+// for this wave's LDS accesses only (LDS data handed to other waves);
+// barrier_phase() only aligns the waves (no data exchanged through it).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void barrier_phase() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Row of key / query m inside a 32-row tile held by accumulator register r.

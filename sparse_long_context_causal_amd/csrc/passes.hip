@@ -12,9 +12,10 @@
 // per KV head g):
 //   * wave g keeps the 32 x d query tiles of its G heads in VGPRs for the
 //     whole launch (MFMA B operands, 16-byte chunks per lane);
-//   * 32-row key tiles of KV head g stream through the wave's own LDS slot
-//     by direct global->LDS loads issued one tile ahead (no VGPRs held), and
-//     are read back as MFMA A operands;
+//   * 32-row key tiles of KV head g stream through the wave's own LDS slots
+//     by direct global->LDS loads (no VGPRs held) issued two tiles ahead in
+//     pass 1 (two slots) and one tile ahead in pass 2, and are read back as
+//     MFMA A operands;
 //   * the G heads are software pipelined inside the wave: the MFMAs of head
 //     h+1 are issued before the exp/sum work of head h, so the matrix core
 //     and the VALU run side by side;
@@ -115,12 +116,16 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   const int ntiles = (n + 31) >> 5;
   const int qt = ntiles - 1 - (int)blockIdx.x;
   const int q0 = qt << 5;
-  unsigned char* slot = smem + wave * KT::kBytes;
+  // two LDS slots per wave: key tile t+2 streams in while tile t is used
+  unsigned char* slot0 = smem + (2 * wave) * KT::kBytes;
+  unsigned char* slot1 = slot0 + KT::kBytes;
   if (blockIdx.x == 0 && threadIdx.x == 0 && zero_counter) *zero_counter = 0;
 
-  issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot);
   uint4 qc[G][NC];
   load_q_tiles<T, D, G>(Q, min(q0 + col, n - 1), hq, g, lane, qc);
+  wait_vmem_all();   // Q in registers before the DMA stream starts
+  issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot0);
+  issue_k_tile<T, D>(K, n, hkv, g, min(1, qt) << 5, lane, slot1);
   float mrun[G], lrun[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -149,11 +154,14 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
     lrun[h] = fmaf(lrun[h], fast_exp2((mrun[h] - mnew) * c), s0 + s1);
     mrun[h] = mnew;
   };
+  // Each tile issues exactly NC DMA ops (the tile two ahead, clamped to the
+  // diagonal), so waiting for <= NC in flight means tile kt has landed.
   auto tile = [&](int kt, bool diag) {
     uint4 kc[NC];
-    wait_vmem_all();
+    unsigned char* slot = (kt & 1) ? slot1 : slot0;
+    wait_vmem_below<NC>();
     read_k_tile<T, D>(slot, lane, kc);
-    if (kt < qt) issue_k_tile<T, D>(K, n, hkv, g, (kt + 1) << 5, lane, slot);
+    issue_k_tile<T, D>(K, n, hkv, g, min(kt + 2, qt) << 5, lane, slot);
     f32x16 a0, a1;
     score_tile<T, NC>(a0, kc, qc[0]);
 #pragma unroll
@@ -165,6 +173,7 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   };
   for (int kt = 0; kt < qt; ++kt) tile(kt, false);
   tile(qt, true);
+  wait_vmem_all();   // the last (clamped) prefetch must land before the LDS is released
 
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       (lpq == 64 ? ~0ull : ((1ull << lpq) - 1ull)) << ((lane / lpq) * lpq);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   unsigned* own_hist = hist + own_n * kFBinWords;
-  __syncthreads();
+  barrier_lds();
 
   // head-summed probabilities of one key tile for this lane's query
   auto tile_mass = [&](int kt, bool diag, float (&pacc)[16]) {
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       float* pb = part + (kt & 1) * part_floats;
 #pragma unroll
       for (int r = 0; r < 16; ++r) pb[part_index(g, r, lane)] = pacc[r];
-      __syncthreads();
+      barrier_lds();   // partial masses visible; the key prefetch keeps streaming
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       const int bt = rs.btau[own_n];
       const bool live = own_q < n && rs.cnt[own_n] <= cap;
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         float* pb = part + (b & 1) * part_floats;
         if (hf == 0) pb[g * 32 + col] = blk;
         blk = 0.f;
-        __syncthreads();
+        barrier_lds();
         if (own_j == 0 && own_q < n) {
           float p = 0.f;
           for (int gg = 0; gg < hkv; ++gg) p += pb[gg * 32 + own_n];
@@ -353,6 +362,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       }
     }
   }
+  wait_vmem_all();
   __syncthreads();
   if (threadIdx.x < 32) {
     const int qq = q0 + threadIdx.x;
@@ -371,7 +381,7 @@ static hipError_t run_pass1(const LayerShape& s, const void* q, const void* k, f
                             int* zero_counter, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
   const float tau = s.scale;
-  const size_t lds = (size_t)s.hkv * KTile<T, D>::kBytes;
+  const size_t lds = (size_t)2 * s.hkv * KTile<T, D>::kBytes;
   auto kern = pass1_lse_kernel<T, D, G>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
