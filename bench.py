@@ -92,7 +92,11 @@ def cpu_baseline(w, x, k, key_block, budget_s=25.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    rows = sample_rows(w, n=x["q"].shape[0])
+    n = x["q"].shape[0]
+    # a seeded uniform row sample, visited in seeded random order until the
+    # time budget is spent (so any prefix of it is itself a uniform sample)
+    rows = sample_rows(w, n=n, count=min(n, 4096))
+    rows = np.random.default_rng(w.row_seed + 1).permutation(rows)
     layer = OracleLayer(x["q"], x["k"], x["v"])
     ix = IndexerOracle(x["q_idx"], x["k_idx"]) if w.indexer_d else None
     done, t_rows = [], 0.0
@@ -107,7 +111,6 @@ def cpu_baseline(w, x, k, key_block, budget_s=25.0):
         done.append(int(i))
         if t_rows > budget_s:
             break
-    n = x["q"].shape[0]
     done = np.asarray(done)
     full_s = t_rows * (n * (n + 1) / 2.0) / float(np.sum(done + 1))
     return {"value": n / full_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
@@ -125,7 +128,7 @@ def main():
     ap.add_argument("--workload", default="long_bf16_32k")
     ap.add_argument("--k", type=int, default=None, help="budget (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run one plain device copy of MB megabytes (to scale HBM "
                          "traffic counters) and exit")

@@ -39,6 +39,16 @@ __device__ __forceinline__ int mass_bin(float p) {
   return min(max(b, 0), kNumBins - 1);
 }
 
+// Filter bins of the pass-2 streaming bound: 8 per octave from 2^-48 to
+// 2^1 (everything smaller shares bin 0). Bin b > 0 starts at mass bit
+// pattern (b + kFBinBase) << kBinShift.
+constexpr int kFBinBase = (127 - 48) << 3;
+constexpr int kFBins = 49 * 8;
+
+__device__ __forceinline__ unsigned filter_bin_floor_bits(int b) {
+  return b > 0 ? (unsigned)(b + kFBinBase) << kBinShift : 0u;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {

@@ -41,10 +41,8 @@
 
 namespace amtk {
 
-// Mass bins for the filter: 8 per octave from 2^-48 to 2^1, u16 counts
-// packed two per LDS word. Masses below 2^-48 share bin 0.
-constexpr int kFBinBase = (127 - 48) << 3;
-constexpr int kFBins = 49 * 8;
+// Mass bins of the filter (kFBins, 8 per octave), u16 counts packed two
+// per LDS word.
 constexpr int kFBinWords = kFBins / 2;
 
 __device__ __forceinline__ int filter_bin(float p) {

@@ -8,10 +8,15 @@
 //
 // Two kernels:
 //   * select_pool_kernel: one workgroup per row picks the top-k from the
-//     row's candidate pool (pass 2 output) by radix select on the fp32 mass
-//     bits (4 rounds of 8 bits, LDS histograms), breaks an exact-value tie by
-//     a second radix select on the unit id, compacts the winners and
-//     bitonic-sorts them by id in LDS.
+//     row's candidate pool (pass 2 output). It first keeps the entries at or
+//     above the row's final bound bin (a superset of the top-k, since every
+//     top-k unit lies in a bin >= the final bound) and copies them to LDS
+//     with wave-ballot compaction. A radix select on the fp32 mass bits then
+//     runs in LDS, starting at the highest bit where the kept values differ
+//     (8-bit digits, LDS histograms); an exact-value tie at the boundary is
+//     broken by a second radix select on the unit id. The winners are
+//     compacted and bitonic-sorted by id in LDS. Rows with more survivors
+//     than the LDS holds select straight from the pool in global memory.
 //   * dense_row_kernel: rows whose pool overflowed are recomputed from Q/K
 //     and pass 1's LSE into a dense per-row mass array (one row per
 //     workgroup, persistent over the overflow list), then selected the same
@@ -22,13 +27,16 @@
 namespace amtk {
 
 constexpr int kSelThreads = 256;
+constexpr int kSelLds = 4096;   // candidates held in LDS by the fast path
 
 struct SelectSmem {
   unsigned hist[256];
   int scal[8];
-  unsigned key[kMaxBudget];
-  unsigned val[kMaxBudget];
+  // fast path: [0] kept masses, [1] kept ids, [2] winner ids, [3] winner masses;
+  // global path: winner ids in [0..1] and masses in [2..3] (kMaxBudget each)
+  unsigned buf[4][kSelLds];
 };
+static_assert(2 * kSelLds >= kMaxBudget, "winner buffers must hold the largest budget");
 
 // Pool entries: (mass bits, unit id) pairs.
 struct PoolView {
@@ -42,19 +50,30 @@ struct DenseView {
   __device__ __forceinline__ unsigned val(int t) const { return __float_as_uint(p[t]); }
   __device__ __forceinline__ unsigned id(int t) const { return (unsigned)t; }
 };
+// Candidates staged in LDS.
+struct LdsView {
+  const unsigned* v;
+  const unsigned* i;
+  __device__ __forceinline__ unsigned val(int t) const { return v[t]; }
+  __device__ __forceinline__ unsigned id(int t) const { return i[t]; }
+};
 
 // Finds, among elements with pred(t), the `need`-th largest of key(t) (a
 // 32-bit unsigned key), by 8-bit radix rounds from the top. Returns the key
 // value; *above is the number of such elements with a strictly larger key
 // and *equal the number with exactly that key. All threads return the same.
+// Digits are 8 bits from bit position top_shift down to 0; bits above
+// top_shift + 8 must be common to all keys (they are taken from `common`).
 template <class KeyFn, class PredFn>
 __device__ unsigned radix_kth_largest(int nc, int need, KeyFn key, PredFn pred, SelectSmem& sm,
-                                      int* above, int* equal) {
+                                      int* above, int* equal, int top_shift = 24,
+                                      unsigned common = 0u) {
   const int tid = threadIdx.x;
-  unsigned prefix = 0u, pmask = 0u;
+  unsigned pmask = top_shift + 8 >= 32 ? 0u : ~((1u << (top_shift + 8)) - 1u);
+  unsigned prefix = common & pmask;
   int higher = 0;
   int eq = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = top_shift; shift >= 0; shift -= 8) {
     sm.hist[tid] = 0u;
     __syncthreads();
     for (int t = tid; t < nc; t += kSelThreads) {
@@ -110,7 +129,8 @@ __device__ unsigned radix_kth_largest(int nc, int need, KeyFn key, PredFn pred, 
 // *out_count = k_eff. Requires nc >= k_eff (every unit of the top-k present).
 template <class View>
 __device__ void select_row(View v, int nc, int k_eff, int kout, int32_t* out_idx,
-                           float* out_mass, int32_t* out_count, SelectSmem& sm) {
+                           float* out_mass, int32_t* out_count, SelectSmem& sm, unsigned* wkey,
+                           unsigned* wval, int top_shift = 24, unsigned common = 0u) {
   const int tid = threadIdx.x;
   unsigned vstar = 0u, istar = 0xffffffffu;
   bool take_all = nc <= k_eff;
@@ -119,7 +139,7 @@ __device__ void select_row(View v, int nc, int k_eff, int kout, int32_t* out_idx
     int above = 0, equal = 0;
     vstar = radix_kth_largest(
         nc, k_eff, [&](int t) { return v.val(t); }, [&](int) { return true; }, sm, &above,
-        &equal);
+        &equal, top_shift, common);
     const int need_eq = k_eff - above;
     if (need_eq < equal) {
       // exact-value tie at the boundary: the smallest ids win
@@ -139,8 +159,8 @@ __device__ void select_row(View v, int nc, int k_eff, int kout, int32_t* out_idx
     if (sel) {
       const int p = atomicAdd(&sm.scal[3], 1);
       if (p < kMaxBudget) {
-        sm.key[p] = id;
-        sm.val[p] = x;
+        wkey[p] = id;
+        wval[p] = x;
       }
     }
   }
@@ -149,8 +169,8 @@ __device__ void select_row(View v, int nc, int k_eff, int kout, int32_t* out_idx
   int S = 1;
   while (S < got) S <<= 1;
   for (int t = got + tid; t < S; t += kSelThreads) {
-    sm.key[t] = 0xffffffffu;
-    sm.val[t] = 0u;
+    wkey[t] = 0xffffffffu;
+    wval[t] = 0u;
   }
   __syncthreads();
   for (int size = 2; size <= S; size <<= 1) {
@@ -159,21 +179,21 @@ __device__ void select_row(View v, int nc, int k_eff, int kout, int32_t* out_idx
         const int lo = 2 * t - (t & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
-        const unsigned a = sm.key[lo], b = sm.key[hi];
+        const unsigned a = wkey[lo], b = wkey[hi];
         if ((a > b) == up) {
-          sm.key[lo] = b;
-          sm.key[hi] = a;
-          const unsigned va = sm.val[lo];
-          sm.val[lo] = sm.val[hi];
-          sm.val[hi] = va;
+          wkey[lo] = b;
+          wkey[hi] = a;
+          const unsigned va = wval[lo];
+          wval[lo] = wval[hi];
+          wval[hi] = va;
         }
       }
       __syncthreads();
     }
   }
   for (int t = tid; t < kout; t += kSelThreads) {
-    out_idx[t] = t < got ? (int32_t)sm.key[t] : -1;
-    if (out_mass) out_mass[t] = t < got ? __uint_as_float(sm.val[t]) : 0.f;
+    out_idx[t] = t < got ? (int32_t)wkey[t] : -1;
+    if (out_mass) out_mass[t] = t < got ? __uint_as_float(wval[t]) : 0.f;
   }
   if (tid == 0) *out_count = got;
   __syncthreads();
@@ -184,16 +204,70 @@ __device__ __forceinline__ int visible_units(int i, int key_block) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_pool_kernel(
-    const uint2* __restrict__ cand, const int* __restrict__ cand_count, int n, int cap,
-    int key_block, int budget, int32_t* __restrict__ idx, int32_t* __restrict__ count,
-    float* __restrict__ mass) {
+    const uint2* __restrict__ cand, const int* __restrict__ cand_count,
+    const int* __restrict__ row_bin, int n, int cap, int key_block, int budget,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ mass) {
   __shared__ SelectSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = n - 1 - (int)blockIdx.x;
   const int nc = cand_count[i];
   if (nc > cap) return;   // overflowed: dense_row_kernel owns this row
   const int k_eff = min(budget, visible_units(i, key_block));
-  select_row(PoolView{cand + (size_t)i * cap}, nc, k_eff, budget, idx + (size_t)i * budget,
-             mass ? mass + (size_t)i * budget : nullptr, count + i, sm);
+  const uint2* pool = cand + (size_t)i * cap;
+  int32_t* out_idx = idx + (size_t)i * budget;
+  float* out_mass = mass ? mass + (size_t)i * budget : nullptr;
+
+  // keep the entries at or above the row's final bound bin, staged in LDS
+  const unsigned floor_bits = filter_bin_floor_bits(row_bin[i]);
+  if (tid == 0) {
+    sm.scal[4] = 0;
+    sm.scal[5] = 0;            // OR of kept masses
+    sm.scal[6] = ~0;           // AND of kept masses
+  }
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  unsigned vor = 0u, vand = ~0u;
+  for (int b0 = 0; b0 < nc; b0 += kSelThreads) {
+    const int t = b0 + tid;
+    uint2 e = make_uint2(0u, 0u);
+    if (t < nc) e = pool[t];
+    const bool keep = t < nc && e.x >= floor_bits;
+    const unsigned long long m = __ballot(keep);
+    int off = 0;
+    if (lane == 0 && m) off = atomicAdd(&sm.scal[4], __popcll(m));
+    off = __shfl(off, 0, 64);
+    if (keep) {
+      const int pos = off + __popcll(m & below);
+      if (pos < kSelLds) {
+        sm.buf[0][pos] = e.x;
+        sm.buf[1][pos] = e.y;
+      }
+      vor |= e.x;
+      vand &= e.x;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    vor |= __shfl_xor(vor, o, 64);
+    vand &= __shfl_xor(vand, o, 64);
+  }
+  if (lane == 0) {
+    atomicOr(reinterpret_cast<unsigned*>(&sm.scal[5]), vor);
+    atomicAnd(reinterpret_cast<unsigned*>(&sm.scal[6]), vand);
+  }
+  __syncthreads();
+  const int kept = sm.scal[4];
+  const unsigned diff = (unsigned)sm.scal[5] ^ (unsigned)sm.scal[6];
+  const unsigned common = (unsigned)sm.scal[6];
+  (void)wave;
+  if (kept <= kSelLds && k_eff <= kSelLds) {
+    const int hb = diff ? 31 - __clz(diff) : 0;   // highest differing bit
+    select_row(LdsView{sm.buf[0], sm.buf[1]}, kept, k_eff, budget, out_idx, out_mass,
+               count + i, sm, sm.buf[2], sm.buf[3], 8 * (hb / 8), common);
+  } else {
+    __syncthreads();
+    select_row(PoolView{pool}, nc, k_eff, budget, out_idx, out_mass, count + i, sm, &sm.buf[0][0],
+               &sm.buf[2][0]);
+  }
 }
 
 // Dense per-row mass for overflow rows: P(u) = sum over the unit's keys of
@@ -244,7 +318,8 @@ __global__ __launch_bounds__(kSelThreads) void dense_row_kernel(
     __syncthreads();
     const int k_eff = min(budget, units);
     select_row(DenseView{P}, units, k_eff, budget, idx + (size_t)i * budget,
-               mass ? mass + (size_t)i * budget : nullptr, count + i, sm);
+               mass ? mass + (size_t)i * budget : nullptr, count + i, sm, &sm.buf[0][0],
+               &sm.buf[2][0]);
   }
 }
 
@@ -264,7 +339,7 @@ hipError_t launch_select(const LayerShape& s, int key_block, int budget, const v
                          const void* k, const float* lse, const CandidatePool& pool, int32_t* idx,
                          int32_t* count, float* mass, hipStream_t stream) {
   hipLaunchKernelGGL(select_pool_kernel, dim3(s.n), dim3(kSelThreads), 0, stream, pool.cand,
-                     pool.count, s.n, pool.cap, key_block, budget, idx, count, mass);
+                     pool.count, pool.bin, s.n, pool.cap, key_block, budget, idx, count, mass);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units_max = key_block == 1 ? s.n : (s.n - 1) / key_block + 1;
