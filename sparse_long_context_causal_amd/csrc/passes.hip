@@ -34,8 +34,10 @@
 // lie in bins >= b_tau (or b_tau = 0). Every unit of the final top-k is
 // therefore >= the bound when it is seen and is kept. Kept units are appended
 // to the row's candidate pool in global memory; the select kernel then picks
-// the exact top-k from the pool. A pool that overflows its capacity is
-// detected (the count keeps running) and the row is redone densely.
+// the exact top-k from the pool. Each row's pool is appended in increasing
+// unit id, so the select kernel emits ascending ids without sorting. A pool
+// that overflows its capacity is detected (the count keeps running) and the
+// row is redone densely.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -308,13 +310,17 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       const int bt = rs.btau[own_n];
       const bool live = own_q < n && rs.cnt[own_n] <= cap;
       int pos = rs.cnt[own_n];
+      // Lane j of a row's lane group takes the row's keys k0 + m with
+      // m = e*lpq + j, so each ballot round appends in increasing key order
+      // and, tile after tile, every row's pool is sorted by key. Key offset m
+      // sits in accumulator register r = 4*(m/8) + m%4 of lane half (m/4)%2.
       for (int e = 0; e < epl; ++e) {
-        const int f = e * lpq + own_j;
-        const int r = f & 15, h2 = f >> 4;
+        const int mo = e * lpq + own_j;
+        const int r = ((mo >> 3) << 2) | (mo & 3), h2 = (mo >> 2) & 1;
         float p = 0.f;
         for (int gg = 0; gg < hkv; ++gg) p += pb[part_index(gg, r, own_n + 32 * h2)];
         p *= inv_hq;
-        const int key = k0 + acc_row(r, h2);
+        const int key = k0 + mo;
         const int bin = filter_bin(p);
         const bool flag = own_q < n && key <= own_q && bin >= bt;
         const unsigned long long m = __ballot(flag) & grp_mask;

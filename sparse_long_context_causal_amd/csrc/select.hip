@@ -7,33 +7,27 @@
 // masses go to the smaller unit id (a fixed, deterministic order).
 //
 // Two kernels:
-//   * select_pool_kernel: one workgroup per row picks the top-k from the
-//     row's candidate pool (pass 2 output). It first keeps the entries at or
-//     above the row's final bound bin (a superset of the top-k, since every
-//     top-k unit lies in a bin >= the final bound) and copies them to LDS
-//     with wave-ballot compaction. A radix select on the fp32 mass bits then
-//     runs in LDS, starting at the highest bit where the kept values differ
-//     (8-bit digits, LDS histograms); an exact-value tie at the boundary is
-//     broken by a second radix select on the unit id. The winners are
-//     compacted and bitonic-sorted by id in LDS. Rows with more survivors
-//     than the LDS holds select straight from the pool in global memory.
+//   * select_wave_kernel: one wave per row picks the top-k from the row's
+//     candidate pool (pass 2 output), which pass 2 appends in increasing unit
+//     id; the selection keeps that order, so ids come out ascending without
+//     a sort (details at the kernel).
 //   * dense_row_kernel: rows whose pool overflowed are recomputed from Q/K
 //     and pass 1's LSE into a dense per-row mass array (one row per
-//     workgroup, persistent over the overflow list), then selected the same
-//     way. It is exact for any input, including massive ties.
+//     workgroup, persistent over the overflow list), then selected by a
+//     workgroup radix select and a bitonic sort by id. It is exact for any
+//     input, including massive ties.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace amtk {
 
 constexpr int kSelThreads = 256;
-constexpr int kSelLds = 4096;   // candidates held in LDS by the fast path
+constexpr int kSelLds = 4096;
 
 struct SelectSmem {
   unsigned hist[256];
   int scal[8];
-  // fast path: [0] kept masses, [1] kept ids, [2] winner ids, [3] winner masses;
-  // global path: winner ids in [0..1] and masses in [2..3] (kMaxBudget each)
+  // winner ids in buf[0..1] and masses in buf[2..3] (kMaxBudget each)
   unsigned buf[4][kSelLds];
 };
 static_assert(2 * kSelLds >= kMaxBudget, "winner buffers must hold the largest budget");
@@ -49,13 +43,6 @@ struct DenseView {
   const float* p;
   __device__ __forceinline__ unsigned val(int t) const { return __float_as_uint(p[t]); }
   __device__ __forceinline__ unsigned id(int t) const { return (unsigned)t; }
-};
-// Candidates staged in LDS.
-struct LdsView {
-  const unsigned* v;
-  const unsigned* i;
-  __device__ __forceinline__ unsigned val(int t) const { return v[t]; }
-  __device__ __forceinline__ unsigned id(int t) const { return i[t]; }
 };
 
 // Finds, among elements with pred(t), the `need`-th largest of key(t) (a
@@ -203,12 +190,30 @@ __device__ __forceinline__ int visible_units(int i, int key_block) {
   return key_block == 1 ? i + 1 : i / key_block + 1;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_pool_kernel(
+// One wave per row. Pass 2 appends each row's pool in increasing unit id,
+// and every step below keeps that order, so the output needs no sort.
+//   1. Stream the pool once and keep the entries at or above the floor of
+//      the row's final bound bin (every top-k unit is among them, and so is
+//      every unit of equal mass), staged in LDS in pool order with
+//      order-preserving ballot compaction.
+//   2. Find the k-th largest mass bit pattern v* exactly: with the kept
+//      masses in registers, fix its bits from the highest one where the kept
+//      masses differ downwards, keeping a bit when at least k kept masses are
+//      >= the prefix with that bit set (a popcount of ballots per step).
+//   3. Walk the kept entries in order and emit those above v*, plus the first
+//      (k - #above) entries equal to v*: equal masses go to the smaller ids.
+// Rows that keep more than the LDS holds run step 2 as an 8-bit radix select
+// over the pool in global memory (LDS histogram) and step 3 over the pool.
+template <int R>
+__global__ __launch_bounds__(64) void select_wave_kernel(
     const uint2* __restrict__ cand, const int* __restrict__ cand_count,
     const int* __restrict__ row_bin, int n, int cap, int key_block, int budget,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ mass) {
-  __shared__ SelectSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kCap = 64 * R;   // kept entries the LDS holds
+  constexpr int U = 8;           // pool loads in flight per lane
+  __shared__ unsigned sv[kCap];
+  __shared__ unsigned si[kCap];
+  const int lane = threadIdx.x;
   const int i = n - 1 - (int)blockIdx.x;
   const int nc = cand_count[i];
   if (nc > cap) return;   // overflowed: dense_row_kernel owns this row
@@ -216,58 +221,169 @@ __global__ __launch_bounds__(kSelThreads) void select_pool_kernel(
   const uint2* pool = cand + (size_t)i * cap;
   int32_t* out_idx = idx + (size_t)i * budget;
   float* out_mass = mass ? mass + (size_t)i * budget : nullptr;
-
-  // keep the entries at or above the row's final bound bin, staged in LDS
+  const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const unsigned floor_bits = filter_bin_floor_bits(row_bin[i]);
-  if (tid == 0) {
-    sm.scal[4] = 0;
-    sm.scal[5] = 0;            // OR of kept masses
-    sm.scal[6] = ~0;           // AND of kept masses
-  }
-  __syncthreads();
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // ---- 1. keep and stage
+  int kept = 0;
   unsigned vor = 0u, vand = ~0u;
-  for (int b0 = 0; b0 < nc; b0 += kSelThreads) {
-    const int t = b0 + tid;
-    uint2 e = make_uint2(0u, 0u);
-    if (t < nc) e = pool[t];
-    const bool keep = t < nc && e.x >= floor_bits;
-    const unsigned long long m = __ballot(keep);
-    int off = 0;
-    if (lane == 0 && m) off = atomicAdd(&sm.scal[4], __popcll(m));
-    off = __shfl(off, 0, 64);
-    if (keep) {
-      const int pos = off + __popcll(m & below);
-      if (pos < kSelLds) {
-        sm.buf[0][pos] = e.x;
-        sm.buf[1][pos] = e.y;
+  for (int b0 = 0; b0 < nc; b0 += 64 * U) {
+    uint2 e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = b0 + 64 * u + lane;
+      e[u] = t < nc ? pool[t] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool keep = b0 + 64 * u + lane < nc && e[u].x >= floor_bits;
+      const unsigned long long m = __ballot(keep);
+      if (keep) {
+        const int pos = kept + __popcll(m & below);
+        if (pos < kCap) {
+          sv[pos] = e[u].x;
+          si[pos] = e[u].y;
+        }
+        vor |= e[u].x;
+        vand &= e[u].x;
       }
-      vor |= e.x;
-      vand &= e.x;
+      kept += __popcll(m);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
     vor |= __shfl_xor(vor, o, 64);
     vand &= __shfl_xor(vand, o, 64);
   }
-  if (lane == 0) {
-    atomicOr(reinterpret_cast<unsigned*>(&sm.scal[5]), vor);
-    atomicAnd(reinterpret_cast<unsigned*>(&sm.scal[6]), vand);
-  }
+  const unsigned diff = vor ^ vand;
+  const int hb = diff ? 31 - __clz(diff) : -1;   // highest bit where kept masses differ
   __syncthreads();
-  const int kept = sm.scal[4];
-  const unsigned diff = (unsigned)sm.scal[5] ^ (unsigned)sm.scal[6];
-  const unsigned common = (unsigned)sm.scal[6];
-  (void)wave;
-  if (kept <= kSelLds && k_eff <= kSelLds) {
-    const int hb = diff ? 31 - __clz(diff) : 0;   // highest differing bit
-    select_row(LdsView{sm.buf[0], sm.buf[1]}, kept, k_eff, budget, out_idx, out_mass,
-               count + i, sm, sm.buf[2], sm.buf[3], 8 * (hb / 8), common);
+
+  int out = 0, eq_seen = 0;
+  // emits entry (x, id) of a 64-entry group in order; valid marks real entries
+  auto emit = [&](bool valid, unsigned x, unsigned id, unsigned vstar, int need_eq) {
+    const unsigned long long em = __ballot(valid && x == vstar);
+    const bool sel = valid && (x > vstar || (x == vstar && eq_seen + __popcll(em & below) < need_eq));
+    const unsigned long long sm = __ballot(sel);
+    if (sel) {
+      const int p = out + __popcll(sm & below);
+      out_idx[p] = (int32_t)id;
+      if (out_mass) out_mass[p] = __uint_as_float(x);
+    }
+    out += __popcll(sm);
+    eq_seen += __popcll(em);
+  };
+
+  if (kept <= kCap) {
+    // ---- 2. exact k-th largest over the kept masses held in registers
+    unsigned v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int t = 64 * r + lane;
+      v[r] = t < kept ? sv[t] : 0u;
+    }
+    // number of kept masses >= x, for x > 0 (padding holds 0)
+    auto count_ge = [&](unsigned x) {
+      int c = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (64 * r >= kept) break;
+        c += __popcll(__ballot(v[r] >= x));
+      }
+      return c;
+    };
+    unsigned vstar = 0u;
+    int need_eq = kept;   // keep everything when kept == k_eff
+    if (kept > k_eff) {
+      vstar = vand;
+      if (hb >= 0) {
+        vstar = hb == 31 ? 0u : (vand & ~((2u << hb) - 1u));
+        for (int b = hb; b >= 0; --b) {
+          const unsigned t = vstar | (1u << b);
+          if (count_ge(t) >= k_eff) vstar = t;
+        }
+      }
+      need_eq = k_eff - count_ge(vstar + 1u);
+    }
+    // ---- 3. emit in order
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (64 * r >= kept) break;
+      const int t = 64 * r + lane;
+      emit(t < kept, v[r], t < kept ? si[t] : 0u, vstar, need_eq);
+    }
   } else {
-    __syncthreads();
-    select_row(PoolView{pool}, nc, k_eff, budget, out_idx, out_mass, count + i, sm, &sm.buf[0][0],
-               &sm.buf[2][0]);
+    // ---- 2'. radix select over the pool in global memory
+    unsigned* hist = sv;   // 256 bins
+    const int top_shift = 8 * (hb / 8);
+    unsigned pmask = top_shift + 8 >= 32 ? 0u : ~((1u << (top_shift + 8)) - 1u);
+    unsigned prefix = vand & pmask;
+    int higher = 0;
+    for (int shift = top_shift; shift >= 0; shift -= 8) {
+      for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+      __syncthreads();
+      for (int b0 = 0; b0 < nc; b0 += 64 * U) {
+        unsigned x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int t = b0 + 64 * u + lane;
+          x[u] = t < nc ? pool[t].x : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (b0 + 64 * u + lane < nc && (x[u] & pmask) == prefix)
+            atomicAdd(&hist[(x[u] >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      // lane L holds bins 4L..4L+3; a suffix sum over lanes finds the digit
+      const unsigned h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+      const unsigned h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+      const int lsum = (int)(h0 + h1 + h2 + h3);
+      int incl = lsum;   // bins of lanes >= this one
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(incl, off, 64);
+        if (lane + off < 64) incl += o;
+      }
+      const int excl = incl - lsum;
+      const int want = k_eff - higher;
+      const bool hit = excl < want && incl >= want;
+      int d = 4 * lane, acc = excl;
+      if (hit) {
+        const unsigned hv[4] = {h0, h1, h2, h3};
+        for (int b = 3; b >= 0; --b) {
+          if (acc + (int)hv[b] >= want) {
+            d = 4 * lane + b;
+            break;
+          }
+          acc += (int)hv[b];
+        }
+      }
+      const int src = __ffsll((long long)__ballot(hit)) - 1;
+      d = __shfl(d, src, 64);
+      acc = __shfl(acc, src, 64);
+      higher += acc;
+      prefix |= (unsigned)d << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    const unsigned vstar = prefix;
+    const int need_eq = k_eff - higher;
+    // ---- 3'. emit in pool order
+    for (int b0 = 0; b0 < nc && out < k_eff; b0 += 64 * U) {
+      uint2 e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = b0 + 64 * u + lane;
+        e[u] = t < nc ? pool[t] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) emit(b0 + 64 * u + lane < nc, e[u].x, e[u].y, vstar, need_eq);
+    }
   }
+  for (int t = k_eff + lane; t < budget; t += 64) {
+    out_idx[t] = -1;
+    if (out_mass) out_mass[t] = 0.f;
+  }
+  if (lane == 0) count[i] = k_eff;
 }
 
 // Dense per-row mass for overflow rows: P(u) = sum over the unit's keys of
@@ -338,8 +454,13 @@ static hipError_t run_dense(const LayerShape& s, int key_block, int budget, cons
 hipError_t launch_select(const LayerShape& s, int key_block, int budget, const void* q,
                          const void* k, const float* lse, const CandidatePool& pool, int32_t* idx,
                          int32_t* count, float* mass, hipStream_t stream) {
-  hipLaunchKernelGGL(select_pool_kernel, dim3(s.n), dim3(kSelThreads), 0, stream, pool.cand,
-                     pool.count, pool.bin, s.n, pool.cap, key_block, budget, idx, count, mass);
+  // LDS rows per lane: room for about 2.5k kept entries (the top k plus the
+  // rest of the boundary bin); rows keeping more take the global-memory path.
+  auto kern = 5 * budget <= 2 * 1024   ? select_wave_kernel<16>
+              : 5 * budget <= 2 * 2048 ? select_wave_kernel<32>
+                                       : select_wave_kernel<64>;
+  hipLaunchKernelGGL(kern, dim3(s.n), dim3(64), 0, stream, pool.cand, pool.count, pool.bin, s.n,
+                     pool.cap, key_block, budget, idx, count, mass);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units_max = key_block == 1 ? s.n : (s.n - 1) / key_block + 1;

@@ -78,8 +78,9 @@ def test_budget_at_least_row_length_is_dense(gpu_lib):
         assert np.max(np.abs(res["out"][i] - layer.dense(i))) <= TOL_OUT["bf16"]
 
 
-def test_equal_keys_tie_to_smallest_ids(gpu_lib):
-    n, hq, hkv, d = 120, 8, 2, 64
+@pytest.mark.parametrize("n", [120, 3000])   # 3000: rows keep more than the select's LDS holds
+def test_equal_keys_tie_to_smallest_ids(gpu_lib, n):
+    hq, hkv, d = 8, 2, 64
     rng = np.random.default_rng(3)
     q = rng.standard_normal((n, hq, d)).astype(np.float32)
     k = np.broadcast_to(rng.standard_normal((1, hkv, d)), (n, hkv, d)).astype(np.float32).copy()
@@ -87,6 +88,53 @@ def test_equal_keys_tie_to_smallest_ids(gpu_lib):
     res = _run_oracle_prefill(gpu_lib, {"q": q, "k": k, "v": v}, "f32", 10)
     for i in range(n):
         assert res["idx"][i][: res["count"][i]].tolist() == list(range(min(10, i + 1)))
+
+
+def _class_keys(n, hq, hkv, d, probs, logits, seed):
+    """Every key is one of a few class vectors (a class per token), and every
+    query head points along its KV head's direction, so row i's logits are
+    about logits[c] for a key of class c, identical within a class, and the
+    classes' masses sit a factor e apart."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((hkv, d))
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    cls = rng.choice(len(probs), size=n, p=probs)
+    t = np.asarray(logits, dtype=np.float64)
+    k = (t[cls][:, None, None] * w[None]).astype(np.float32)
+    g_of_h = np.arange(hq) // (hq // hkv)
+    q = (np.sqrt(d) * w[g_of_h][None] + 0.05 * rng.standard_normal((n, hq, d))).astype(np.float32)
+    v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    return {"q": q, "k": k, "v": v}, cls
+
+
+@pytest.mark.parametrize("n,k,probs", [
+    (4000, 300, [0.02, 0.03, 0.45, 0.5]),
+    (5000, 700, [0.02, 0.10, 0.45, 0.43]),
+])
+def test_key_classes_exact_supports(gpu_lib, n, k, probs):
+    """Supports follow from the construction: whole classes in order of
+    logit, then the smallest ids of the class holding the k-th unit. Long
+    rows keep whole classes beyond what the select's LDS holds, short ones
+    fit; both select paths see several distinct masses and exact ties."""
+    logits = [3.0, 2.0, 1.0, 0.0]
+    x, cls = _class_keys(n, 8, 2, 64, probs, logits, seed=n + k)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in (n // 3, n - 1):   # the construction's class order holds in the oracle
+        sc = layer.row(i, k)["score"]
+        per = [sc[np.nonzero(cls[: i + 1] == c)[0]] for c in range(4)]
+        assert all(p.size and np.ptp(p) <= 1e-12 * p.max() for p in per)
+        assert per[0][0] > per[1][0] > per[2][0] > per[3][0]
+    res = _run_oracle_prefill(gpu_lib, x, "f32", k)
+    for i in range(n):
+        want = []
+        for c in range(4):
+            ids = np.nonzero(cls[: i + 1] == c)[0]
+            want.extend(ids[: k - len(want)].tolist())
+            if len(want) == k:
+                break
+        want = sorted(want)
+        assert res["count"][i] == len(want), f"row {i}"
+        assert res["idx"][i][: len(want)].tolist() == want, f"row {i}"
 
 
 def test_overflow_path_gives_same_supports(gpu_lib):
