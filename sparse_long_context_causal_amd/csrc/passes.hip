@@ -16,9 +16,11 @@
 //     by direct global->LDS loads (no VGPRs held) issued two tiles ahead in
 //     pass 1 (two slots) and one tile ahead in pass 2, and are read back as
 //     MFMA A operands;
-//   * the G heads are software pipelined inside the wave: the MFMAs of head
-//     h+1 are issued before the exp/sum work of head h, so the matrix core
-//     and the VALU run side by side;
+//   * pass 1 pipelines the G heads inside the wave (the MFMAs of head h+1
+//     are issued before the exp/sum work of head h); pass 2 pipelines key
+//     tiles instead (tile t+1's first MFMAs are issued before tile t's
+//     barrier and row-owner phase). Two waves per SIMD let one wave's MFMAs
+//     overlap the other's exponentials;
 //   * the diagonal tile (causal mask) is peeled out of the main loop;
 //   * pass 1 keeps an online max / sum per (head, query) in registers;
 //   * pass 2 turns logits into probabilities with pass 1's LSE, sums the G
@@ -262,54 +264,71 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   const int own_n = wave * qpw + lane / lpq;       // tile-local row this lane serves
   const int own_j = lane % lpq;
   const int own_q = q0 + own_n;
+  const bool own_ok = own_q < n;
   const unsigned long long grp_mask =
       (lpq == 64 ? ~0ull : ((1ull << lpq) - 1ull)) << ((lane / lpq) * lpq);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   unsigned* own_hist = hist + own_n * kFBinWords;
   barrier_lds();
 
-  // head-summed probabilities of one key tile for this lane's query
-  auto tile_mass = [&](int kt, bool diag, float (&pacc)[16]) {
-    uint4 kc[NC];
+  // Software pipeline over key tiles: tile kt+1 is read from LDS and its
+  // first head's MFMAs are issued before tile kt's barrier, so the matrix
+  // core works through the barrier wait and the row-owner phase.
+  uint4 kc[NC];
+  f32x16 a0;
+  auto load_k = [&](int kt) {   // key tile kt is in the slot; start tile kt+1
     wait_vmem_all();
     read_k_tile<T, D>(slot, lane, kc);
     if (kt < qt) issue_k_tile<T, D>(K, n, hkv, g, (kt + 1) << 5, lane, slot);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
-    f32x16 a0, a1;
-    score_tile<T, NC>(a0, kc, qc[0]);
+  };
+  // head-summed probabilities of the current key tile for this lane's query
+  // (head 0's scores are already in a0). Heads run one after the other on
+  // one accumulator: the other wave on the SIMD overlaps its MFMAs with this
+  // wave's exponentials, and the registers saved keep Q resident.
+  auto tile_mass = [&](bool diag, float (&pacc)[16]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (h + 1 < G) score_tile<T, NC>((h & 1) ? a0 : a1, kc, qc[h + 1]);
-      const f32x16& a = (h & 1) ? a1 : a0;
+      if (h > 0) score_tile<T, NC>(a0, kc, qc[h]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pacc[r] += fast_exp2(fmaf(a[r], c, -bias[h]));
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(a0[r], c, -bias[h]));
+        pacc[r] = h == 0 ? e : pacc[r] + e;
+      }
     }
-    if (!diag) interleave_mfma_valu<NC * ChunkMma<T>::kSteps, (G - 1) * NC * ChunkMma<T>::kSteps, 48 / (NC * ChunkMma<T>::kSteps)>();
     if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (acc_row(r, hf) > col) pacc[r] = 0.f;
     }
   };
+  load_k(0);
+  score_tile<T, NC>(a0, kc, qc[0]);
 
   float blk = 0.f;   // KB > 1: this query's mass over the current key block (this wave's heads)
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
     float pacc[16];
-    if (diag) tile_mass(kt, true, pacc);
-    else tile_mass(kt, false, pacc);
+    if (diag) tile_mass(true, pacc);
+    else tile_mass(false, pacc);
 
     if constexpr (KB == 1) {
       float* pb = part + (kt & 1) * part_floats;
 #pragma unroll
       for (int r = 0; r < 16; ++r) pb[part_index(g, r, lane)] = pacc[r];
-      barrier_lds();   // partial masses visible; the key prefetch keeps streaming
+      if (!diag) {
+        load_k(kt + 1);
+        score_tile<T, NC>(a0, kc, qc[0]);
+      }
+      barrier_lds();   // partial masses visible; the next tile's MFMAs run on
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
+      // A mass passes the bound bin exactly when its bit pattern is at least
+      // the bin's floor pattern, so the bin itself is only formed for the
+      // histogram of appended entries.
       const int bt = rs.btau[own_n];
-      const bool live = own_q < n && rs.cnt[own_n] <= cap;
+      const unsigned thr = filter_bin_floor_bits(bt);
       int pos = rs.cnt[own_n];
+      const bool live = own_ok && pos <= cap;
       // Lane j of a row's lane group takes the row's keys k0 + m with
       // m = e*lpq + j, so each ballot round appends in increasing key order
       // and, tile after tile, every row's pool is sorted by key. Key offset m
@@ -317,21 +336,30 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       for (int e = 0; e < epl; ++e) {
         const int mo = e * lpq + own_j;
         const int r = ((mo >> 3) << 2) | (mo & 3), h2 = (mo >> 2) & 1;
-        float p = 0.f;
-        for (int gg = 0; gg < hkv; ++gg) p += pb[part_index(gg, r, own_n + 32 * h2)];
+        const float* src = pb + part_index(0, r, own_n + 32 * h2);
+        float p = src[0];   // summed over KV heads in a fixed order
+        if (hkv == 8) {
+#pragma unroll
+          for (int gg = 1; gg < 8; ++gg) p += src[gg * 16 * 64];
+        } else {
+          for (int gg = 1; gg < hkv; ++gg) p += src[gg * 16 * 64];
+        }
         p *= inv_hq;
+        const unsigned bits = __float_as_uint(p);
         const int key = k0 + mo;
-        const int bin = filter_bin(p);
-        const bool flag = own_q < n && key <= own_q && bin >= bt;
+        const bool flag = own_ok && bits >= thr && (!diag || key <= own_q);
         const unsigned long long m = __ballot(flag) & grp_mask;
         if (flag) {
           const int at = pos + __popcll(m & below);
-          if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(__float_as_uint(p), (unsigned)key);
-          if (live) atomicAdd(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
+          if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(bits, (unsigned)key);
+          if (live) {
+            const int bin = filter_bin(p);
+            atomicAdd(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
+          }
         }
         pos += __popcll(m);
       }
-      if (own_j == 0 && own_q < n) {
+      if (own_j == 0 && own_ok) {
         rs.cnt[own_n] = pos;
         if (pos <= cap) raise_bound(rs, own_hist, own_n, budget);
       }
@@ -342,6 +370,10 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       for (int r = 0; r < 16; ++r) ps += pacc[r];
       ps += xor32f(ps);
       blk += ps;
+      if (!diag) {
+        load_k(kt + 1);
+        score_tile<T, NC>(a0, kc, qc[0]);
+      }
       if ((kt & 1) || diag) {
         const int b = kt >> 1;
         float* pb = part + (b & 1) * part_floats;
