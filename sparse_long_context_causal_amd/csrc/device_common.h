@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace amtk {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -124,8 +126,18 @@ struct ChunkMma<float> {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ void dma_chunk(const void* gsrc, void* lds_slot_chunk) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)lds_slot_chunk, 16, 0, 0);
+// Chunk c of a key tile: the instruction's immediate offset (16*c) moves
+// both the global and the LDS address, so one lane address serves every
+// chunk and the LDS base (M0, wave-uniform) is slot + 1008*c, which puts the
+// chunk at slot + 1024*c.
+template <int C>
+__device__ __forceinline__ void dma_chunk(const void* gsrc, unsigned char* slot) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)(slot + (1024 - 16) * C), 16, 16 * C, 0);
+}
+template <int... Cs>
+__device__ __forceinline__ void dma_chunks(const void* gsrc, unsigned char* slot,
+                                           std::integer_sequence<int, Cs...>) {
+  (dma_chunk<Cs>(gsrc, slot), ...);
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -66,8 +66,7 @@ __device__ __forceinline__ void issue_k_tile(const T* __restrict__ K, int n, int
   const int row = min(k0 + (lane & 31), n - 1);
   const unsigned char* src = reinterpret_cast<const unsigned char*>(
       K + ((size_t)row * hkv + g) * D + (lane >> 5) * (D / 2));
-#pragma unroll
-  for (int c = 0; c < KT::kChunks; ++c) dma_chunk(src + 16 * c, slot + 1024 * c);
+  dma_chunks(src, slot, std::make_integer_sequence<int, KT::kChunks>{});
 }
 
 template <typename T, int D>
@@ -111,7 +110,7 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   typedef KTile<T, D> KT;
   constexpr int NC = KT::kChunks;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
   const int g = wave;
   const int hq = hkv * G;
@@ -194,6 +193,14 @@ struct RowState {
   int btau[32];   // current bound bin
 };
 
+// LDS add without return, as an explicit instruction: as a plain atomic the
+// compiler would make it wait for every outstanding global load (vmcnt(0)),
+// including the key tile streaming into LDS.
+__device__ __forceinline__ void lds_add(unsigned* p, unsigned x) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(x) : "memory");
+}
+
+
 // Raise the row's bound while more than k candidates lie strictly above it.
 __device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* words, int r,
                                             int budget) {
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   const int part_floats = (KB == 1) ? hkv * 16 * 64 : hkv * 32;           // one buffer
   unsigned char* slots = reinterpret_cast<unsigned char*>(part + 2 * part_floats);
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
   const int g = wave;
   const int hq = hkv * G;
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
           if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(bits, (unsigned)key);
           if (live) {
             const int bin = filter_bin(p);
-            atomicAdd(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
+            lds_add(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
           }
         }
         pos += __popcll(m);

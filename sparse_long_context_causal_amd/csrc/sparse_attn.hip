@@ -316,12 +316,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
     }
     l = fmaf(l, alpha, ps);
     m = mnew;
-    float a4[4];
-    gather4(alpha, b2, a4);
+    // The output rescale is skipped when no head's running maximum moved:
+    // every factor is then exactly 1.
+    if (__ballot(alpha != 1.0f)) {
+      float a4[4];
+      gather4(alpha, b2, a4);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] *= a4[h];
+        for (int e = 0; e < E; ++e) acc[h][e] *= a4[h];
+    }
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       float p4[4];
