@@ -128,36 +128,48 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot0);
   issue_k_tile<T, D>(K, n, hkv, g, min(1, qt) << 5, lane, slot1);
   float mrun[G], lrun[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mrun[h] = kNegBig;
-    lrun[h] = 0.f;
-  }
 
-  // exp/sum work of one head on its score tile (16 keys x 1 query per lane)
-  auto stats = [&](f32x16& acc, int h, bool diag) {
-    if (diag) {
+  // exp/sum work of one head on its score tile (16 keys x 1 query per lane).
+  // With a running maximum (kTrack) as in a streaming softmax; without it,
+  // the lane's maximum over the first key tile stays the reference for the
+  // rest of the row, which saves the per-element maximum. Terms far below
+  // the reference underflow harmlessly next to its own weight of 1; a logit
+  // more than ~127 (in log2 units) above it overflows the sum to infinity,
+  // which the caller detects and redoes with a running maximum.
+  auto stats = [&](f32x16& acc, int h, auto diag_c, auto track_c) {
+    if constexpr (decltype(diag_c)::value) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (acc_row(r, hf) > col) acc[r] = -INFINITY;
     }
-    float tmax = fmaxf(acc[0], acc[1]);
+    if constexpr (decltype(track_c)::value) {
+      float tmax = fmaxf(acc[0], acc[1]);
 #pragma unroll
-    for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
-    const float mnew = fmaxf(mrun[h], tmax);
-    const float mc = mnew * c;
-    float s0 = 0.f, s1 = 0.f;
+      for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+      const float mnew = fmaxf(mrun[h], tmax);
+      const float mc = mnew * c;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      s0 += fast_exp2(fmaf(acc[r], c, -mc));
-      s1 += fast_exp2(fmaf(acc[r + 1], c, -mc));
+      for (int r = 0; r < 16; r += 2) {
+        s0 += fast_exp2(fmaf(acc[r], c, -mc));
+        s1 += fast_exp2(fmaf(acc[r + 1], c, -mc));
+      }
+      lrun[h] = fmaf(lrun[h], fast_exp2((mrun[h] - mnew) * c), s0 + s1);
+      mrun[h] = mnew;
+    } else {
+      const float mc = mrun[h] * c;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        s0 += fast_exp2(fmaf(acc[r], c, -mc));
+        s1 += fast_exp2(fmaf(acc[r + 1], c, -mc));
+      }
+      lrun[h] += s0 + s1;
     }
-    lrun[h] = fmaf(lrun[h], fast_exp2((mrun[h] - mnew) * c), s0 + s1);
-    mrun[h] = mnew;
   };
   // Each tile issues exactly NC DMA ops (the tile two ahead, clamped to the
   // diagonal), so waiting for <= NC in flight means tile kt has landed.
-  auto tile = [&](int kt, bool diag) {
+  auto tile = [&](int kt, auto diag_c, auto track_c) {
     uint4 kc[NC];
     unsigned char* slot = (kt & 1) ? slot1 : slot0;
     wait_vmem_below<NC>();
@@ -168,13 +180,38 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (h + 1 < G) score_tile<T, NC>((h & 1) ? a0 : a1, kc, qc[h + 1]);
-      stats((h & 1) ? a1 : a0, h, diag);
+      stats((h & 1) ? a1 : a0, h, diag_c, track_c);
     }
-    if (!diag) interleave_mfma_valu<NC * ChunkMma<T>::kSteps, (G - 1) * NC * ChunkMma<T>::kSteps, 64 / (NC * ChunkMma<T>::kSteps)>();
+    if constexpr (!decltype(diag_c)::value)
+      interleave_mfma_valu<NC * ChunkMma<T>::kSteps, (G - 1) * NC * ChunkMma<T>::kSteps, 64 / (NC * ChunkMma<T>::kSteps)>();
   };
-  for (int kt = 0; kt < qt; ++kt) tile(kt, false);
-  tile(qt, true);
-  wait_vmem_all();   // the last (clamped) prefetch must land before the LDS is released
+  using yes = std::true_type;
+  using no = std::false_type;
+  // one pass over the row's key tiles (tiles 0 and 1 already in flight)
+  auto sweep = [&](auto track_c) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mrun[h] = kNegBig;
+      lrun[h] = 0.f;
+    }
+    if (qt == 0) {
+      tile(0, yes{}, yes{});
+    } else {
+      tile(0, no{}, yes{});   // the reference: tile 0 with a running maximum
+      for (int kt = 1; kt < qt; ++kt) tile(kt, no{}, track_c);
+      tile(qt, yes{}, track_c);
+    }
+    wait_vmem_all();   // the last (clamped) prefetch must land before the slots are reused
+  };
+  sweep(no{});
+  bool over = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) over |= !(lrun[h] < INFINITY);
+  if (__ballot(over)) {   // rare: redo the wave's rows with a running maximum
+    issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot0);
+    issue_k_tile<T, D>(K, n, hkv, g, min(1, qt) << 5, lane, slot1);
+    sweep(yes{});
+  }
 
 #pragma unroll
   for (int h = 0; h < G; ++h) {

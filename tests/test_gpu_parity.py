@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import OracleLayer, IndexerOracle, tokens_of_blocks
-from synth import WORKLOADS, generate, random_inputs, sample_rows
+from synth import WORKLOADS, generate, random_inputs, round_bf16, sample_rows
 from tests.gpu_helpers import (BAND, TOL_LSE, TOL_OUT, check_outputs_on_gpu_support,
                                check_support_rows, upload)
 
@@ -135,6 +135,35 @@ def test_key_classes_exact_supports(gpu_lib, n, k, probs):
         want = sorted(want)
         assert res["count"][i] == len(want), f"row {i}"
         assert res["idx"][i][: len(want)].tolist() == want, f"row {i}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lse_far_above_first_key_tile(gpu_lib, dtype):
+    """One key (id 100) scores about 180 log2 units above every key of the
+    first 32-key tile, so a sum referenced to the first tile's maximum would
+    overflow; rows that see it must still match the oracle (their LSE is
+    about 125, so fp32 keeps ~1e-5 there: the check allows 4 ulp on top)."""
+    n, hq, hkv, d = 200, 8, 2, 64
+    rng = np.random.default_rng(77)
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    q = (25.0 * e0 + 0.01 * rng.standard_normal((n, hq, d))).astype(np.float32)
+    k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    k[100] = 40.0 * e0
+    v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    x = {"q": q, "k": k, "v": v}
+    layer = OracleLayer(q, k, v)
+    res = _run_oracle_prefill(gpu_lib, x, dtype, 8)
+    for i in range(n):
+        ref = layer.row(i, 8)["lse"]
+        tol = TOL_LSE[dtype] + 4 * np.spacing(np.abs(ref).astype(np.float32))
+        assert np.all(np.abs(res["lse"][:, i] - ref) <= tol), f"lse row {i}"
+    assert np.all(res["idx"][100:, :8] >= 0) and np.all(np.any(res["idx"][100:] == 100, axis=1))
+    check_support_rows(res["idx"], res["count"], layer, np.arange(n), 8)
+    check_outputs_on_gpu_support(res["out"], None, layer, np.arange(0, n, 3), res["idx"],
+                                 res["count"], 1, dtype)
 
 
 def test_overflow_path_gives_same_supports(gpu_lib):
