@@ -22,6 +22,7 @@ namespace amtk {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef uint16_t bf16_t;   // bf16 storage
 
 constexpr float kLog2e = 1.4426950408889634f;

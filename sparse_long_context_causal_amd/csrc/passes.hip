@@ -40,6 +40,8 @@
 // unit id, so the select kernel emits ascending ids without sorting. A pool
 // that overflows its capacity is detected (the count keeps running) and the
 // row is redone densely.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -63,10 +65,13 @@ template <typename T, int D>
 __device__ __forceinline__ void issue_k_tile(const T* __restrict__ K, int n, int hkv, int g,
                                              int k0, int lane, unsigned char* slot) {
   typedef KTile<T, D> KT;
-  const int row = min(k0 + (lane & 31), n - 1);
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(
-      K + ((size_t)row * hkv + g) * D + (lane >> 5) * (D / 2));
-  dma_chunks(src, slot, std::make_integer_sequence<int, KT::kChunks>{});
+  // wave-uniform tile base + a 32-bit lane offset (row lane%32, d half
+  // lane/32), so the loads take the scalar-base form
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(K + ((size_t)k0 * hkv + g) * D);
+  int row = lane & 31;
+  if (k0 + 31 >= n) row = min(row, n - 1 - k0);   // a tile past the last key repeats it
+  const unsigned off = (unsigned)((row * hkv * D + (lane >> 5) * (D / 2)) * (int)sizeof(T));
+  dma_chunks(base + off, slot, std::make_integer_sequence<int, KT::kChunks>{});
 }
 
 template <typename T, int D>
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   // the reference underflow harmlessly next to its own weight of 1; a logit
   // more than ~127 (in log2 units) above it overflows the sum to infinity,
   // which the caller detects and redoes with a running maximum.
-  auto stats = [&](f32x16& acc, int h, auto diag_c, auto track_c) {
+  auto stats = [&](f32x16& acc, int h, auto diag_c, auto track_c) __attribute__((always_inline)) {
     if constexpr (decltype(diag_c)::value) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   };
   // Each tile issues exactly NC DMA ops (the tile two ahead, clamped to the
   // diagonal), so waiting for <= NC in flight means tile kt has landed.
-  auto tile = [&](int kt, auto diag_c, auto track_c) {
+  auto tile = [&](int kt, auto diag_c, auto track_c) __attribute__((always_inline)) {
     uint4 kc[NC];
     unsigned char* slot = (kt & 1) ? slot1 : slot0;
     wait_vmem_below<NC>();
@@ -187,30 +192,125 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   };
   using yes = std::true_type;
   using no = std::false_type;
-  // one pass over the row's key tiles (tiles 0 and 1 already in flight)
-  auto sweep = [&](auto track_c) {
+
+  // Interleaved schedule for the fixed-reference tiles (bf16, even G): one
+  // MFMA of the next head, then the exp/sum work of 16/NC elements of the
+  // current head, and so on, so one wave keeps the matrix core and the VALU
+  // busy together (left alone, the compiler issues the MFMAs in bursts that
+  // stall the wave). The order is held by empty volatile asm statements
+  // (which keep their program order): each one makes the next MFMA's key
+  // operand and the next group's inputs depend on the previous group's sums.
+  // The sums are formed in the same order as in stats(), so results match.
+  constexpr bool kInterleave = std::is_same<T, bf16_t>::value && (G % 2 == 0);
+  constexpr int kEpg = 16 / NC;   // elements of the current head per MFMA
+  auto step = [&](f32x16& nxt, uint4 (&kk)[NC], const uint4 (&qq)[NC], const f32x16& cur,
+                  int h) __attribute__((always_inline)) {
+    const float mc = mrun[h] * c;
+    float s0 = 0.f, s1 = 0.f;
+    nxt = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      float x[kEpg];
+#pragma unroll
+      for (int e = 0; e < kEpg; ++e) x[e] = cur[cc * kEpg + e];
+      u32x4 kv = __builtin_bit_cast(u32x4, kk[cc]);
+      if constexpr (kEpg == 2)
+        asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]) : "v"(s0), "v"(s1));
+      else
+        asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "v"(s0), "v"(s1));
+      kk[cc] = __builtin_bit_cast(uint4, kv);
+      ChunkMma<T>::mma(nxt, kk[cc], qq[cc]);
+#pragma unroll
+      for (int e = 0; e < kEpg; ++e) {
+        const int r = cc * kEpg + e;
+        const float y = fast_exp2(fmaf(x[e], c, -mc));
+        if (r & 1) s1 += y;
+        else s0 += y;
+      }
+    }
+    lrun[h] += s0 + s1;
+  };
+  // exp/sum work of one head with no MFMA beside it (fixed reference)
+  auto tail = [&](const f32x16& cur, int h) __attribute__((always_inline)) {
+    const float mc = mrun[h] * c;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      s0 += fast_exp2(fmaf(cur[r], c, -mc));
+      s1 += fast_exp2(fmaf(cur[r + 1], c, -mc));
+    }
+    lrun[h] += s0 + s1;
+  };
+  // key tile kt lands in registers (DMA accounting as in tile())
+  auto load_tile = [&](int kt, uint4 (&kk)[NC]) __attribute__((always_inline)) {
+    unsigned char* slot = (kt & 1) ? slot1 : slot0;
+    wait_vmem_below<NC>();
+    // the previous MFMAs read their key operands at issue; keep a margin
+    // before the LDS read overwrites those registers
+    asm volatile("s_nop 15" ::: "memory");
+    read_k_tile<T, D>(slot, lane, kk);
+    issue_k_tile<T, D>(K, n, hkv, g, min(kt + 2, qt) << 5, lane, slot);
+  };
+  auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       mrun[h] = kNegBig;
       lrun[h] = 0.f;
     }
-    if (qt == 0) {
-      tile(0, yes{}, yes{});
-    } else {
-      tile(0, no{}, yes{});   // the reference: tile 0 with a running maximum
-      for (int kt = 1; kt < qt; ++kt) tile(kt, no{}, track_c);
-      tile(qt, yes{}, track_c);
-    }
-    wait_vmem_all();   // the last (clamped) prefetch must land before the slots are reused
   };
-  sweep(no{});
+  // One pass over the row's key tiles (tiles 0 and 1 are already in flight):
+  // tile 0 sets the reference, tiles 1 .. qt-1 use it (interleaved schedule
+  // where available), then the diagonal tile.
+  reset();
+  if (qt == 0) {
+    tile(0, yes{}, yes{});
+  } else {
+    tile(0, no{}, yes{});
+    if constexpr (kInterleave) {
+      if (qt >= 2) {
+        uint4 kc[NC];
+        f32x16 a0, a1;
+        load_tile(1, kc);
+        score_tile<T, NC>(a0, kc, qc[0]);
+        for (int kt = 1; kt < qt; ++kt) {
+          const bool more = kt + 1 < qt;   // the next tile is interleaved too
+          // head h beside head h+1 (G even: head h's scores are in a0 for
+          // even h, a1 for odd h); the last head beside the next tile's head 0
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            f32x16& cur = (h & 1) ? a1 : a0;
+            f32x16& nxt = (h & 1) ? a0 : a1;
+            if (h + 1 < G) {
+              step(nxt, kc, qc[h + 1], cur, h);
+            } else if (more) {
+              load_tile(kt + 1, kc);
+              step(nxt, kc, qc[0], cur, h);
+            } else {
+              tail(cur, h);
+            }
+          }
+        }
+      }
+    } else {
+      for (int kt = 1; kt < qt; ++kt) tile(kt, no{}, no{});
+    }
+    tile(qt, yes{}, no{});
+  }
+  wait_vmem_all();   // the last (clamped) prefetch must land before the slots are reused
   bool over = false;
 #pragma unroll
   for (int h = 0; h < G; ++h) over |= !(lrun[h] < INFINITY);
   if (__ballot(over)) {   // rare: redo the wave's rows with a running maximum
     issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot0);
     issue_k_tile<T, D>(K, n, hkv, g, min(1, qt) << 5, lane, slot1);
-    sweep(yes{});
+    reset();
+    if (qt == 0) {
+      tile(0, yes{}, yes{});
+    } else {
+      for (int kt = 0; kt < qt; ++kt) tile(kt, no{}, yes{});
+      tile(qt, yes{}, yes{});
+    }
+    wait_vmem_all();
   }
 
 #pragma unroll
