@@ -91,13 +91,29 @@ struct Mma<float> {
 // ------------------------------------------------------ K tiles through LDS
 // A wave stages a 32-row key tile for one KV head in its own LDS slot with
 // direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land
-// at slot + 16*l), so the prefetch holds no VGPRs. Each lane loads the half
-// row its MFMA A operand needs (row l%32, d half l/32) as kChunks 16-byte
-// chunks; chunk c of every lane forms the 1 KiB block slot + 1024*c.
+// at M0 + 16*l), so the prefetch holds no VGPRs. Each lane's MFMA A operand
+// is row l%32, d half l/32, as kChunks 16-byte chunks.
 template <typename T, int D>
 struct KTile {
   static constexpr int kChunks = (D / 2) * (int)sizeof(T) / 16;   // 16 B chunks per lane
   static constexpr int kBytes = kChunks * 1024;                   // LDS bytes per slot
+};
+
+// Layout of a key tile in its slot. A key row is kCpr 16-byte chunks; each
+// DMA instruction c loads kRpi whole rows (c*kRpi ..), so its 64 lanes read
+// contiguous rows and every cache line they touch is used in full. Chunk j
+// of tile row r sits at 16-byte position r*kCpr + (j ^ sw(r)); the XOR
+// spreads the 16 rows read together by an MFMA operand load over all 16
+// bank groups. DMA lane l of instruction c lands at position 64*c + l, i.e.
+// row c*kRpi + l/kCpr, chunk (l%kCpr) ^ sw(row); that lane offset repeats
+// with period kPer in c and is computed once (KLane).
+template <typename T, int D>
+struct KLayout {
+  static constexpr int kCpr = D * (int)sizeof(T) / 16;
+  static constexpr int kRpi = 64 / kCpr;
+  static constexpr int kNc = kCpr / 2;                 // = KTile::kChunks
+  static constexpr int kPer = kCpr == 8 ? 2 : (kCpr == 16 ? 4 : 8);
+  __device__ __forceinline__ static int sw(int r) { return kCpr == 8 ? (r >> 1) & 7 : r & 15; }
 };
 
 // MFMA over one 16-byte chunk per lane of A and B: one 32x32x16 bf16 step,
@@ -127,20 +143,6 @@ struct ChunkMma<float> {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Chunk c of a key tile: the instruction's immediate offset (16*c) moves
-// both the global and the LDS address, so one lane address serves every
-// chunk and the LDS base (M0, wave-uniform) is slot + 1008*c, which puts the
-// chunk at slot + 1024*c.
-template <int C>
-__device__ __forceinline__ void dma_chunk(const void* gsrc, unsigned char* slot) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_ptr_t)(slot + (1024 - 16) * C), 16, 16 * C, 0);
-}
-template <int... Cs>
-__device__ __forceinline__ void dma_chunks(const void* gsrc, unsigned char* slot,
-                                           std::integer_sequence<int, Cs...>) {
-  (dma_chunk<Cs>(gsrc, slot), ...);
-}
-
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Waits until at most N vector-memory operations of this wave are in flight
@@ -154,21 +156,77 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
 
-// Reads 4 consecutive 1 KiB chunks (this lane's 16 bytes of each) and waits
-// for them inside the same asm block. The outputs are early-clobber ("=&v"):
-// a load that lands while later loads of the block are still being issued
-// must not overwrite the address register they use.
-__device__ __forceinline__ void lds_read4(uint32_t addr, uint4& a, uint4& b, uint4& c, uint4& d) {
+// Reads 4 16-byte chunks (one address each) and waits for them inside the
+// same asm block. The outputs are early-clobber ("=&v"): a load that lands
+// while later loads of the block are still being issued must not overwrite
+// an address register they use.
+__device__ __forceinline__ void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                          uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:1024\n\t"
-      "ds_read_b128 %2, %4 offset:2048\n\t"
-      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
-      : "v"(addr)
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
 }
+
+// Per-lane constants of the key-tile layout for one launch, two VGPRs.
+// The swizzle only flips address bits that the row and slot bases leave
+// clear, so every offset is one of these XOR a compile-time constant:
+//   DMA lane offset of instruction c = d0 ^ (kXs * (c % kPer)),
+//   read address of chunk k (of the lane's half) = (slot + rx) ^ (16 * k),
+// where slots are aligned to a multiple of the row pitch (kCpr * 16 bytes).
+template <typename T, int D>
+struct KLane {
+  typedef KLayout<T, D> L;
+  static constexpr unsigned kXs = 16u * (L::kCpr == 8 ? 4u : (unsigned)L::kRpi);
+  unsigned d0;   // DMA: byte offset from instruction 0's first row
+  unsigned rx;   // read: byte offset of chunk 0 of the lane's half, in a slot
+  __device__ __forceinline__ void init(int lane, int hkv) {
+    const unsigned rs = (unsigned)(hkv * D * (int)sizeof(T));   // global row stride (bytes)
+    d0 = (unsigned)(lane / L::kCpr) * rs + 16u * (unsigned)((lane % L::kCpr) ^ L::sw(lane / L::kCpr));
+    const int r = lane & 31;
+    rx = (unsigned)(r * L::kCpr * 16) | (16u * (unsigned)(((lane >> 5) * L::kNc) ^ L::sw(r)));
+  }
+
+  // DMA of key tile k0 .. k0+31 of KV head g into `slot`. A tile that runs
+  // past the last key repeats key n-1 in its place (those keys are causally
+  // masked or belong to rows past n).
+  __device__ __forceinline__ void issue(const T* K, int n, int hkv, int g, int k0,
+                                        unsigned char* slot) const {
+    const size_t rs = (size_t)hkv * D * sizeof(T);
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(K + ((size_t)k0 * hkv + g) * D);
+    if (k0 + 31 < n) {
+#pragma unroll
+      for (int c = 0; c < L::kNc; ++c)
+        __builtin_amdgcn_global_load_lds(base + (size_t)(c * L::kRpi) * rs + (d0 ^ (kXs * (unsigned)(c % L::kPer))),
+                                         (lds_ptr_t)(slot + 1024 * c), 16, 0, 0);
+    } else {
+      const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+      for (int c = 0; c < L::kNc; ++c) {
+        const int r = c * L::kRpi + lane / L::kCpr;
+        const int rr = min(r, n - 1 - k0);
+        const unsigned off =
+            (unsigned)rr * (unsigned)rs + 16u * (unsigned)((lane % L::kCpr) ^ L::sw(r));
+        __builtin_amdgcn_global_load_lds(base + off, (lds_ptr_t)(slot + 1024 * c), 16, 0, 0);
+      }
+    }
+  }
+
+  // The lane's MFMA A operand chunks (row lane%32, d half lane/32) of the
+  // tile in `slot`.
+  __device__ __forceinline__ void read(const unsigned char* slot, uint4 (&kc)[L::kNc]) const {
+    const uint32_t a = lds_addr(slot) + rx;
+#pragma unroll
+    for (int k = 0; k < L::kNc; k += 4)
+      lds_read4(a ^ (16u * k), a ^ (16u * (k + 1)), a ^ (16u * (k + 2)), a ^ (16u * (k + 3)),
+                kc[k], kc[k + 1], kc[k + 2], kc[k + 3]);
+  }
+};
 
 // Scheduling hint for a software-pipelined tile: the first `lead` MFMAs
 // alone, then one MFMA per `valu` VALU instructions for `pairs` rounds, then

@@ -16,11 +16,9 @@
 //     by direct global->LDS loads (no VGPRs held) issued two tiles ahead in
 //     pass 1 (two slots) and one tile ahead in pass 2, and are read back as
 //     MFMA A operands;
-//   * pass 1 pipelines the G heads inside the wave (the MFMAs of head h+1
-//     are issued before the exp/sum work of head h); pass 2 pipelines key
-//     tiles instead (tile t+1's first MFMAs are issued before tile t's
-//     barrier and row-owner phase). Two waves per SIMD let one wave's MFMAs
-//     overlap the other's exponentials;
+//   * pass 1 interleaves each head's exp/sum work with the next head's
+//     MFMAs inside the wave; in pass 2 the two waves of a SIMD overlap one
+//     wave's MFMAs with the other's exponentials;
 //   * the diagonal tile (causal mask) is peeled out of the main loop;
 //   * pass 1 keeps an online max / sum per (head, query) in registers;
 //   * pass 2 turns logits into probabilities with pass 1's LSE, sums the G
@@ -58,30 +56,6 @@ __device__ __forceinline__ int filter_bin(float p) {
 
 __device__ __forceinline__ int hist_count(const unsigned* words, int b) {
   return (int)((words[b >> 1] >> ((b & 1) * 16)) & 0xffffu);
-}
-
-// ---------------------------------------------------------------- K tiles
-template <typename T, int D>
-__device__ __forceinline__ void issue_k_tile(const T* __restrict__ K, int n, int hkv, int g,
-                                             int k0, int lane, unsigned char* slot) {
-  typedef KTile<T, D> KT;
-  // wave-uniform tile base + a 32-bit lane offset (row lane%32, d half
-  // lane/32), so the loads take the scalar-base form
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(K + ((size_t)k0 * hkv + g) * D);
-  int row = lane & 31;
-  if (k0 + 31 >= n) row = min(row, n - 1 - k0);   // a tile past the last key repeats it
-  const unsigned off = (unsigned)((row * hkv * D + (lane >> 5) * (D / 2)) * (int)sizeof(T));
-  dma_chunks(base + off, slot, std::make_integer_sequence<int, KT::kChunks>{});
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void read_k_tile(const unsigned char* slot, int lane,
-                                            uint4 (&kc)[KTile<T, D>::kChunks]) {
-  typedef KTile<T, D> KT;
-  const uint32_t a = lds_addr(slot) + 16 * lane;
-#pragma unroll
-  for (int c = 0; c < KT::kChunks; c += 4)
-    lds_read4(a + 1024 * c, kc[c], kc[c + 1], kc[c + 2], kc[c + 3]);
 }
 
 template <typename T, int D, int G>
@@ -130,8 +104,10 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   uint4 qc[G][NC];
   load_q_tiles<T, D, G>(Q, min(q0 + col, n - 1), hq, g, lane, qc);
   wait_vmem_all();   // Q in registers before the DMA stream starts
-  issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot0);
-  issue_k_tile<T, D>(K, n, hkv, g, min(1, qt) << 5, lane, slot1);
+  KLane<T, D> kl;
+  kl.init(lane, hkv);
+  kl.issue(K, n, hkv, g, 0, slot0);
+  kl.issue(K, n, hkv, g, min(1, qt) << 5, slot1);
   float mrun[G], lrun[G];
 
   // exp/sum work of one head on its score tile (16 keys x 1 query per lane).
@@ -178,8 +154,8 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
     uint4 kc[NC];
     unsigned char* slot = (kt & 1) ? slot1 : slot0;
     wait_vmem_below<NC>();
-    read_k_tile<T, D>(slot, lane, kc);
-    issue_k_tile<T, D>(K, n, hkv, g, min(kt + 2, qt) << 5, lane, slot);
+    kl.read(slot, kc);
+    kl.issue(K, n, hkv, g, min(kt + 2, qt) << 5, slot);
     f32x16 a0, a1;
     score_tile<T, NC>(a0, kc, qc[0]);
 #pragma unroll
@@ -248,8 +224,8 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
     // the previous MFMAs read their key operands at issue; keep a margin
     // before the LDS read overwrites those registers
     asm volatile("s_nop 15" ::: "memory");
-    read_k_tile<T, D>(slot, lane, kk);
-    issue_k_tile<T, D>(K, n, hkv, g, min(kt + 2, qt) << 5, lane, slot);
+    kl.read(slot, kk);
+    kl.issue(K, n, hkv, g, min(kt + 2, qt) << 5, slot);
   };
   auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -301,8 +277,8 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
 #pragma unroll
   for (int h = 0; h < G; ++h) over |= !(lrun[h] < INFINITY);
   if (__ballot(over)) {   // rare: redo the wave's rows with a running maximum
-    issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot0);
-    issue_k_tile<T, D>(K, n, hkv, g, min(1, qt) << 5, lane, slot1);
+    kl.issue(K, n, hkv, g, 0, slot0);
+    kl.issue(K, n, hkv, g, min(1, qt) << 5, slot1);
     reset();
     if (qt == 0) {
       tile(0, yes{}, yes{});
@@ -356,10 +332,12 @@ __device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* words,
 }
 
 // Swizzled partial-mass layout: element (register r, source lane) of KV head
-// g's tile lives at word r*64 + ((lane + 4r) & 63) of that head's 4 KiB block,
-// so both the lane-major writes and the row-owner reads are bank-conflict free.
+// g's tile lives at word r*64 + (lane ^ 4r) of that head's 4 KiB block, so
+// both the lane-major writes and the row-owner reads are bank-conflict free.
+// The whole index is (g*1024 + lane) ^ (68*r): one base per lane and an XOR
+// with a constant per register.
 __device__ __forceinline__ int part_index(int g, int r, int src_lane) {
-  return (g * 16 + r) * 64 + ((src_lane + 4 * r) & 63);
+  return (g * 16 + r) * 64 + (src_lane ^ (4 * r));
 }
 
 template <typename T, int D, int G, int KB>
@@ -375,7 +353,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   RowState& rs = *reinterpret_cast<RowState*>(hist + 32 * kFBinWords);
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(&rs) + sizeof(RowState));
   const int part_floats = (KB == 1) ? hkv * 16 * 64 : hkv * 32;           // one buffer
-  unsigned char* slots = reinterpret_cast<unsigned char*>(part + 2 * part_floats);
+  // key slots start on a 1 KiB boundary (the key-tile swizzle needs slots
+  // aligned to the row pitch)
+  unsigned char* slots = smem + ((reinterpret_cast<unsigned char*>(part + 2 * part_floats) - smem + 1023) & ~(ptrdiff_t)1023);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
@@ -388,7 +368,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   const int qrow = min(q0 + col, n - 1);
   unsigned char* slot = slots + wave * KT::kBytes;
 
-  issue_k_tile<T, D>(K, n, hkv, g, 0, lane, slot);
+  KLane<T, D> kl;
+  kl.init(lane, hkv);
+  kl.issue(K, n, hkv, g, 0, slot);
   for (int t = threadIdx.x; t < 32 * kFBinWords; t += nthreads) hist[t] = 0u;
   if (threadIdx.x < 32) {
     rs.cnt[threadIdx.x] = 0;
@@ -415,15 +397,12 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   unsigned* own_hist = hist + own_n * kFBinWords;
   barrier_lds();
 
-  // Software pipeline over key tiles: tile kt+1 is read from LDS and its
-  // first head's MFMAs are issued before tile kt's barrier, so the matrix
-  // core works through the barrier wait and the row-owner phase.
   uint4 kc[NC];
   f32x16 a0;
   auto load_k = [&](int kt) {   // key tile kt is in the slot; start tile kt+1
     wait_vmem_all();
-    read_k_tile<T, D>(slot, lane, kc);
-    if (kt < qt) issue_k_tile<T, D>(K, n, hkv, g, (kt + 1) << 5, lane, slot);
+    kl.read(slot, kc);
+    if (kt < qt) kl.issue(K, n, hkv, g, (kt + 1) << 5, slot);
   };
   // head-summed probabilities of the current key tile for this lane's query
   // (head 0's scores are already in a0). Heads run one after the other on
@@ -445,26 +424,22 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         if (acc_row(r, hf) > col) pacc[r] = 0.f;
     }
   };
-  load_k(0);
-  score_tile<T, NC>(a0, kc, qc[0]);
-
   float blk = 0.f;   // KB > 1: this query's mass over the current key block (this wave's heads)
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
+    load_k(kt);
+    score_tile<T, NC>(a0, kc, qc[0]);
     float pacc[16];
     if (diag) tile_mass(true, pacc);
     else tile_mass(false, pacc);
 
     if constexpr (KB == 1) {
       float* pb = part + (kt & 1) * part_floats;
+      const int wb = (kt & 1) * part_floats + g * 1024 + lane;   // = part_index(g, 0, lane) in this buffer
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pb[part_index(g, r, lane)] = pacc[r];
-      if (!diag) {
-        load_k(kt + 1);
-        score_tile<T, NC>(a0, kc, qc[0]);
-      }
-      barrier_lds();   // partial masses visible; the next tile's MFMAs run on
+      for (int r = 0; r < 16; ++r) part[wb ^ (68 * r)] = pacc[r];
+      barrier_lds();   // partial masses visible
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       // A mass passes the bound bin exactly when its bit pattern is at least
       // the bin's floor pattern, so the bin itself is only formed for the
@@ -514,10 +489,6 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       for (int r = 0; r < 16; ++r) ps += pacc[r];
       ps += xor32f(ps);
       blk += ps;
-      if (!diag) {
-        load_k(kt + 1);
-        score_tile<T, NC>(a0, kc, qc[0]);
-      }
       if ((kt & 1) || diag) {
         const int b = kt >> 1;
         float* pb = part + (b & 1) * part_floats;
@@ -576,6 +547,7 @@ template <typename T, int D>
 static size_t pass2_lds_bytes(int hkv, int key_block) {
   size_t b = 32 * kFBinWords * sizeof(unsigned) + sizeof(RowState);
   b += 2 * ((key_block == 1) ? (size_t)hkv * 16 * 64 : (size_t)hkv * 32) * sizeof(float);
+  b = (b + 1023) & ~(size_t)1023;   // key slots on a 1 KiB boundary
   b += (size_t)hkv * KTile<T, D>::kBytes;
   return b;
 }
