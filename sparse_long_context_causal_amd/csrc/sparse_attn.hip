@@ -360,6 +360,206 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
     lse_out[(size_t)(g * G + myh) * n + i] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// MFMA path for bf16, d = 128, 8 KV heads x 4 query heads, key blocks of 1
+// or a multiple of 16 tokens. One wave per query row, the KV heads one after
+// another over the row's support, in chunks of 16 tokens:
+//  * logits: the 4 query heads of KV head g against 16 gathered key rows
+//    with four 16x16x32 bf16 MFMAs (exact products, fp32 sums). Rows of the
+//    A operand repeat the 4 heads, so every 16-lane row of the result holds
+//    s[head r][token lane%16] in register r;
+//  * online softmax per head on those lanes (16-lane DPP max), the running
+//    maximum weighing exactly 1 as in the generic path;
+//  * the fp32 weights of the chunk go through a 256-byte LDS slot to all
+//    lanes; 16-lane row q loads the value rows of tokens q, q+4, q+8, q+12
+//    (16 bytes a lane), lane l accumulates d [8(l%16), +8) of the 4 heads
+//    over its row's tokens in fp32 (P is never rounded), and the 4 rows are
+//    summed once per KV head;
+//  * the (head, chunk) steps form one loop whose next step's key rows,
+//    value pairs and query fragment are loaded while the current one runs.
+// Each lane looks up the token ids of its own key and value rows.
+constexpr int kMfmaWaves = 4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// max / sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_row<0x128>(x));
+  x = fmaxf(x, dpp_row<0x124>(x));
+  x = fmaxf(x, dpp_row<0x122>(x));
+  return fmaxf(x, dpp_row<0x121>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_row<0x128>(x);
+  x += dpp_row<0x124>(x);
+  x += dpp_row<0x122>(x);
+  return x + dpp_row<0x121>(x);
+}
+
+template <bool kUnitTokens>   // true: key_block == 1; false: key_block % 16 == 0
+__global__ __launch_bounds__(64 * kMfmaWaves) void sparse_attn_mfma_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
+    float* __restrict__ lse_out, int n, int key_block, int max_units, float c) {
+  constexpr int D = 128, HKV = 8, G = 4, HQ = HKV * G;
+  __shared__ float4 pbuf[kMfmaWaves][16];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int i = n - 1 - (int)(blockIdx.x * kMfmaWaves + wave);
+  if (i < 0) return;
+  const int tl = lane & 15, qb = lane >> 4;   // token / k block of the MFMA operands
+  const int cnt = min(max(count[i], 0), max_units);
+  const int total = cnt * key_block;
+  const int nch = (total + 15) >> 4;
+  if (nch == 0) {   // empty support: zero output, LSE -inf
+    for (int e = lane; e < HQ * D; e += 64) O[(size_t)i * HQ * D + e] = 0.f;
+    if (lse_out && lane < HQ) lse_out[(size_t)lane * n + i] = -INFINITY;
+    return;
+  }
+  const int32_t* ids = idx + (size_t)i * max_units;
+
+  // token tt of the support: key/value row j (row i stands in for padding)
+  auto token = [&](int tt, int& j) -> bool {
+    bool ok;
+    if constexpr (kUnitTokens) {
+      const int id = ids[min(tt, max_units - 1)];
+      ok = tt < total && id >= 0 && id <= i;
+      j = ok ? id : i;
+    } else {
+      const int u = min(tt / key_block, max_units - 1);
+      const int id = ids[u];
+      const int jj = id * key_block + (tt - u * key_block);
+      ok = tt < total && id >= 0 && jj <= i;
+      j = ok ? jj : i;
+    }
+    return ok;
+  };
+  struct Step {
+    uint4 kf[4];   // key row of token tl, d [32s + 8qb, +8) for s = 0..3
+    uint4 vq[4];   // value row of token 4u + qb, d [8tl, 8tl + 8) for u = 0..3
+    bool okl;      // this lane's key token is valid
+  };
+  auto load_step = [&](int stp, Step& st) {
+    const int g = stp / nch, t0 = (stp - g * nch) << 4;
+    int jl;
+    st.okl = token(t0 + tl, jl);
+    const bf16_t* kr = K + ((size_t)jl * HKV + g) * D + 8 * qb;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) st.kf[s2] = *reinterpret_cast<const uint4*>(kr + 32 * s2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int jv;
+      token(t0 + 4 * u + qb, jv);   // padding tokens weigh 0; the row is valid
+      st.vq[u] = *reinterpret_cast<const uint4*>(V + ((size_t)jv * HKV + g) * D + 8 * tl);
+    }
+  };
+  auto load_q = [&](int g, uint4 (&qf)[4]) {
+    const bf16_t* qr = Q + ((size_t)i * HQ + G * g + (tl & 3)) * D + 8 * qb;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) qf[s2] = *reinterpret_cast<const uint4*>(qr + 32 * s2);
+  };
+
+  uint4 qf[4];
+  float acc[G][8], m[G], lp[G];
+  const int steps = HKV * nch;
+  // one (KV head, chunk) step on loaded data
+  auto run_step = [&](int stp, const Step& cur) {
+    const int g = stp / nch, ch = stp - g * nch;
+    if (ch == 0) {
+      load_q(g, qf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        m[h] = kNegBig;
+        lp[h] = 0.f;
+      }
+    }
+    // logits of the 4 heads for the chunk's 16 tokens
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[s2]),
+                                                   __builtin_bit_cast(bf16x8, cur.kf[s2]), sc, 0, 0, 0);
+    float p[G], alpha[G];
+    bool moved = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float x = cur.okl ? __fmul_rn(sc[h], c) : -INFINITY;
+      const float mnew = fmaxf(m[h], row16_max(x));
+      alpha[h] = m[h] == mnew ? 1.0f : fast_exp2(m[h] - mnew);
+      moved |= m[h] != mnew;
+      // the running maximum weighs exactly 1 (exp2 of 0 is only ~1 ulp exact)
+      p[h] = !cur.okl ? 0.f : (x == mnew ? 1.0f : fast_exp2(x - mnew));
+      m[h] = mnew;
+    }
+    if (moved) {   // uniform: the row maxima are the same in every lane
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+        lp[h] *= alpha[h];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) lp[h] += p[h];
+    if (lane < 16) pbuf[wave][tl] = make_float4(p[0], p[1], p[2], p[3]);
+    __builtin_amdgcn_wave_barrier();
+    float4 pt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pt[u] = pbuf[wave][4 * u + qb];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned w4[4] = {cur.vq[u].x, cur.vq[u].y, cur.vq[u].z, cur.vq[u].w};
+      const float pw[4] = {pt[u].x, pt[u].y, pt[u].z, pt[u].w};
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const float v0 = __uint_as_float(w4[k2] << 16), v1 = __uint_as_float(w4[k2] & 0xffff0000u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][2 * k2] = fmaf(pw[h], v0, acc[h][2 * k2]);
+          acc[h][2 * k2 + 1] = fmaf(pw[h], v1, acc[h][2 * k2 + 1]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ch == nch - 1) {   // head group g done: sum the 4 row groups' tokens
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float l = row16_sum(lp[h]);   // the 16 lanes of a row hold one token each
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float v = acc[h][e];
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          o[e] = v * inv;
+        }
+        if (qb == 0) {
+          float4* op = reinterpret_cast<float4*>(O + ((size_t)i * HQ + G * g + h) * D + 8 * tl);
+          op[0] = make_float4(o[0], o[1], o[2], o[3]);
+          op[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+        if (lse_out && lane == 0)
+          lse_out[(size_t)(G * g + h) * n + i] = l > 0.f ? (m[h] + log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+  };
+  // two step buffers in turn: the next step's loads are in flight meanwhile
+  Step sa, sb;
+  load_step(0, sa);
+  for (int stp = 0; stp < steps; stp += 2) {
+    if (stp + 1 < steps) load_step(stp + 1, sb);
+    run_step(stp, sa);
+    if (stp + 1 >= steps) break;
+    if (stp + 2 < steps) load_step(stp + 2, sa);
+    run_step(stp + 1, sb);
+  }
+}
+
 template <typename T, int E, int G>
 static hipError_t run_attn(const LayerShape& s, int key_block, int max_units, const void* q,
                            const void* k, const void* v, const int32_t* idx,
@@ -419,6 +619,16 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
                               const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream) {
+  if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32 &&
+      (key_block == 1 || key_block % 16 == 0)) {
+    const int blocks = (s.n + kMfmaWaves - 1) / kMfmaWaves;
+    auto kern = key_block == 1 ? sparse_attn_mfma_kernel<true> : sparse_attn_mfma_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kMfmaWaves), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, key_block,
+                       max_units, s.scale * kLog2e);
+    return hipGetLastError();
+  }
   if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32) {
     constexpr int CH = 4;
     const int blocks = (s.n + kAttnWaves - 1) / kAttnWaves;
