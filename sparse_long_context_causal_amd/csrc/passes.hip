@@ -398,7 +398,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   barrier_lds();
 
   uint4 kc[NC];
-  f32x16 a0;
+  f32x16 a0, a1;
   auto load_k = [&](int kt) {   // key tile kt is in the slot; start tile kt+1
     wait_vmem_all();
     kl.read(slot, kc);
@@ -408,14 +408,57 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   // (head 0's scores are already in a0). Heads run one after the other on
   // one accumulator: the other wave on the SIMD overlaps its MFMAs with this
   // wave's exponentials, and the registers saved keep Q resident.
+  // exp/sum work of head h on its scores `cur` into pacc (head 0 assigns)
+  auto head_exps = [&](const f32x16& cur, int h, float (&pacc)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(cur[r], c, -bias[h]));
+      pacc[r] = h == 0 ? e : pacc[r] + e;
+    }
+  };
+  // bf16: the exp/sum work of head h runs beside the MFMAs of head h+1, one
+  // MFMA per 16/NC elements, the order held by empty volatile asm statements
+  // that tie each MFMA's key operand to the previous group's results (as in
+  // pass 1). The per-element sums keep the head order, so results match.
+  constexpr bool kInterleave = std::is_same<T, bf16_t>::value && G >= 2;
+  constexpr int kEpg = 16 / NC;
+  auto head_step = [&](f32x16& nxt, const uint4 (&qq)[NC], const f32x16& cur, int h,
+                       float (&pacc)[16]) __attribute__((always_inline)) {
+    nxt = f32x16{};
+    float last = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      float x[kEpg];
+#pragma unroll
+      for (int e = 0; e < kEpg; ++e) x[e] = cur[cc * kEpg + e];
+      u32x4 kv = __builtin_bit_cast(u32x4, kc[cc]);
+      if constexpr (kEpg == 2)
+        asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]) : "v"(last));
+      else
+        asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "v"(last));
+      kc[cc] = __builtin_bit_cast(uint4, kv);
+      ChunkMma<T>::mma(nxt, kc[cc], qq[cc]);
+#pragma unroll
+      for (int e = 0; e < kEpg; ++e) {
+        const int r = cc * kEpg + e;
+        const float ev = fast_exp2(fmaf(x[e], c, -bias[h]));
+        pacc[r] = h == 0 ? ev : pacc[r] + ev;
+      }
+      last = pacc[cc * kEpg + kEpg - 1];
+    }
+  };
+  // head-summed probabilities of the current key tile for this lane's query
+  // (head 0's scores are already in a0)
   auto tile_mass = [&](bool diag, float (&pacc)[16]) {
+    if constexpr (kInterleave) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (h > 0) score_tile<T, NC>(a0, kc, qc[h]);
+      for (int h = 0; h + 1 < G; ++h) head_step((h & 1) ? a0 : a1, qc[h + 1], (h & 1) ? a1 : a0, h, pacc);
+      head_exps(((G - 1) & 1) ? a1 : a0, G - 1, pacc);
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(a0[r], c, -bias[h]));
-        pacc[r] = h == 0 ? e : pacc[r] + e;
+      for (int h = 0; h < G; ++h) {
+        if (h > 0) score_tile<T, NC>(a0, kc, qc[h]);
+        head_exps(a0, h, pacc);
       }
     }
     if (diag) {
@@ -431,8 +474,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     load_k(kt);
     score_tile<T, NC>(a0, kc, qc[0]);
     float pacc[16];
-    if (diag) tile_mass(true, pacc);
-    else tile_mass(false, pacc);
+    tile_mass(diag, pacc);
 
     if constexpr (KB == 1) {
       float* pb = part + (kt & 1) * part_floats;
