@@ -404,10 +404,6 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     kl.read(slot, kc);
     if (kt < qt) kl.issue(K, n, hkv, g, (kt + 1) << 5, slot);
   };
-  // head-summed probabilities of the current key tile for this lane's query
-  // (head 0's scores are already in a0). Heads run one after the other on
-  // one accumulator: the other wave on the SIMD overlaps its MFMAs with this
-  // wave's exponentials, and the registers saved keep Q resident.
   // exp/sum work of head h on its scores `cur` into pacc (head 0 assigns)
   auto head_exps = [&](const f32x16& cur, int h, float (&pacc)[16]) __attribute__((always_inline)) {
 #pragma unroll
