@@ -362,202 +362,298 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
 
 // ---------------------------------------------------------------------------
 // MFMA path for bf16, d = 128, 8 KV heads x 4 query heads, key blocks of 1
-// or a multiple of 16 tokens. One wave per query row, the KV heads one after
-// another over the row's support, in chunks of 16 tokens:
-//  * logits: the 4 query heads of KV head g against 16 gathered key rows
-//    with four 16x16x32 bf16 MFMAs (exact products, fp32 sums). Rows of the
-//    A operand repeat the 4 heads, so every 16-lane row of the result holds
-//    s[head r][token lane%16] in register r;
-//  * online softmax per head on those lanes (16-lane DPP max), the running
-//    maximum weighing exactly 1 as in the generic path;
-//  * the fp32 weights of the chunk go through a 256-byte LDS slot to all
-//    lanes; 16-lane row q loads the value rows of tokens q, q+4, q+8, q+12
-//    (16 bytes a lane), lane l accumulates d [8(l%16), +8) of the 4 heads
-//    over its row's tokens in fp32 (P is never rounded), and the 4 rows are
-//    summed once per KV head;
-//  * the (head, chunk) steps form one loop whose next step's key rows,
-//    value pairs and query fragment are loaded while the current one runs.
-// Each lane looks up the token ids of its own key and value rows.
-constexpr int kMfmaWaves = 4;
+// or a multiple of 16 tokens. One single-wave workgroup per (query row, KV
+// head), numbered row-major with the KV head fastest: workgroups are handed
+// to the 8 XCDs round robin, so XCD g serves KV head g of every row and its
+// L2 holds the keys and values of that one head (an eighth of the layer).
+// The support is walked in chunks of 32 tokens; a chunk is two sets of 16
+// (sigma = 0, 1), MFMA row m of set sigma being token 16*sigma + m.
+//  * every global read of the loop is a DMA into LDS (no registers, no ALU
+//    work): instruction c of a chunk brings the whole 256-byte key (and
+//    value) rows of tokens 4c .. 4c+3, lane 16w + p taking 16-byte piece
+//    p of row 4c + w; the piece of d-chunk x of row R sits at position
+//    x ^ 2(R & 7) of the row, which keeps both LDS read patterns below
+//    conflict free;
+//  * logits S[token][head] with 16x16x32 bf16 MFMAs (exact products, fp32
+//    sums): A = the key rows (lane l: token l%16, d 32s + 8(l/16) + [0, 8)
+//    for s = 0..3, 16-byte LDS reads); B = the query fragment, column n
+//    holding head n%4. Lane l ends with the logits of head l%4 for tokens
+//    16*sigma + 4(l/16) + r in register r.
+//  * online softmax per head: the maximum of the lane's 8 logits, then over
+//    the 4 lane groups l/16 with two xor shuffles; rescaling only when a
+//    maximum moved.
+//  * P V with 16x16x32 bf16 MFMAs over the chunk's 32 tokens. Each weight
+//    is split into two bf16 numbers, hi = p rounded and lo = (p - hi)
+//    rounded, which keeps about 16 significant bits: A-operand rows 0-3
+//    carry hi of the 4 heads, rows 4-7 lo (rows 8-15 repeat hi and are
+//    never read). With the token order above, a lane's own weights already
+//    sit where the A operand wants them (row l%16, k = 8(l/16) + 4 sigma + r).
+//    B = the value rows through the transposing read ds_read_b64_tr_b16,
+//    which hands every lane V[token][d] for 4 consecutive k. The two row
+//    sums are added at the end.
+//  * a chunk: wait for its loads, copy its keys and values out of LDS,
+//    issue every load of the next chunk into the buffers just freed, then
+//    compute from registers while those are in flight.
+constexpr int kTileBytes = 8192;   // 32 rows of 256 bytes: keys or values of one chunk
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; the other counters left at their maximum)
+constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_row(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+// A chunk's operands out of LDS: key fragment 4*sigma + s = 16-byte read at
+// ka[s] + 4096*sigma; value fragment 2*blk + sigma = transposing read at
+// va[blk] + 4096*sigma. Waits for them inside the same asm block.
+__device__ __forceinline__ void read_chunk(const uint32_t (&ka)[4], const uint32_t (&va)[8],
+                                           u32x4 (&kf)[8], u32x2 (&vt)[16]) {
+  asm volatile(
+      "ds_read_b128 %0, %24\n\t"
+      "ds_read_b128 %1, %25\n\t"
+      "ds_read_b128 %2, %26\n\t"
+      "ds_read_b128 %3, %27\n\t"
+      "ds_read_b128 %4, %24 offset:4096\n\t"
+      "ds_read_b128 %5, %25 offset:4096\n\t"
+      "ds_read_b128 %6, %26 offset:4096\n\t"
+      "ds_read_b128 %7, %27 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %8, %28\n\t"
+      "ds_read_b64_tr_b16 %9, %28 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %29\n\t"
+      "ds_read_b64_tr_b16 %11, %29 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %30\n\t"
+      "ds_read_b64_tr_b16 %13, %30 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %31\n\t"
+      "ds_read_b64_tr_b16 %15, %31 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %16, %32\n\t"
+      "ds_read_b64_tr_b16 %17, %32 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %18, %33\n\t"
+      "ds_read_b64_tr_b16 %19, %33 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %20, %34\n\t"
+      "ds_read_b64_tr_b16 %21, %34 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %22, %35\n\t"
+      "ds_read_b64_tr_b16 %23, %35 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]),
+        "=&v"(kf[6]), "=&v"(kf[7]), "=&v"(vt[0]), "=&v"(vt[1]), "=&v"(vt[2]), "=&v"(vt[3]),
+        "=&v"(vt[4]), "=&v"(vt[5]), "=&v"(vt[6]), "=&v"(vt[7]), "=&v"(vt[8]), "=&v"(vt[9]),
+        "=&v"(vt[10]), "=&v"(vt[11]), "=&v"(vt[12]), "=&v"(vt[13]), "=&v"(vt[14]),
+        "=&v"(vt[15])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+      : "memory");
 }
-// max / sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1)
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_row<0x128>(x));
-  x = fmaxf(x, dpp_row<0x124>(x));
-  x = fmaxf(x, dpp_row<0x122>(x));
-  return fmaxf(x, dpp_row<0x121>(x));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_row<0x128>(x);
-  x += dpp_row<0x124>(x);
-  x += dpp_row<0x122>(x);
-  return x + dpp_row<0x121>(x);
+
+// broadcast of lane (l & ~3) | R to the 4 lanes of each quad
+template <int R>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), R * 0x55, 0xF, 0xF, false));
 }
 
 template <bool kUnitTokens>   // true: key_block == 1; false: key_block % 16 == 0
-__global__ __launch_bounds__(64 * kMfmaWaves) void sparse_attn_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
     float* __restrict__ lse_out, int n, int key_block, int max_units, float c) {
   constexpr int D = 128, HKV = 8, G = 4, HQ = HKV * G;
-  __shared__ float4 pbuf[kMfmaWaves][16];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int i = n - 1 - (int)(blockIdx.x * kMfmaWaves + wave);
-  if (i < 0) return;
-  const int tl = lane & 15, qb = lane >> 4;   // token / k block of the MFMA operands
+  constexpr unsigned kRowBytes = HKV * D * sizeof(bf16_t);   // one token, all KV heads
+  __shared__ __align__(256) unsigned char smem[2 * kTileBytes];   // keys, values of a chunk
+  const int lane = threadIdx.x;
+  const int i = n - 1 - (int)(blockIdx.x / HKV);   // longest rows first
+  const int g = (int)(blockIdx.x % HKV);
+  const int m = lane & 15, q = lane >> 4;
   const int cnt = min(max(count[i], 0), max_units);
   const int total = cnt * key_block;
-  const int nch = (total + 15) >> 4;
+  const int nch = (total + 31) >> 5;
   if (nch == 0) {   // empty support: zero output, LSE -inf
-    for (int e = lane; e < HQ * D; e += 64) O[(size_t)i * HQ * D + e] = 0.f;
-    if (lse_out && lane < HQ) lse_out[(size_t)lane * n + i] = -INFINITY;
+    for (int e = lane; e < G * D; e += 64) O[((size_t)i * HQ + G * g) * D + e] = 0.f;
+    if (lse_out && lane < G) lse_out[(size_t)(G * g + lane) * n + i] = -INFINITY;
     return;
   }
   const int32_t* ids = idx + (size_t)i * max_units;
+  unsigned char* kbuf = smem;
+  unsigned char* vbuf = smem + kTileBytes;
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K) + g * (D * 2);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V) + g * (D * 2);
+  // DMA: lane 16q + m takes piece m of row 4c + q (c = 0..7), which holds
+  // d-chunk m ^ 2((4c + q) & 7): byte offset in the row by the parity of c
+  const unsigned xo0 = 16u * (unsigned)(m ^ (2 * q)), xo1 = 16u * (unsigned)(m ^ (8 + 2 * q));
 
-  // token tt of the support: key/value row j (row i stands in for padding)
-  auto token = [&](int tt, int& j) -> bool {
-    bool ok;
+  // Raw token ids of chunk ch for the lane's DMA rows 4c + q (single
+  // tokens), or the block ids of the chunk's two sets (key blocks: a set
+  // never straddles two blocks; raw[0] and raw[4])
+  auto fetch_ids = [&](int ch, int (&raw)[8]) {
+    const int t0 = ch << 5;
     if constexpr (kUnitTokens) {
-      const int id = ids[min(tt, max_units - 1)];
-      ok = tt < total && id >= 0 && id <= i;
-      j = ok ? id : i;
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) raw[c8] = ids[min(t0 + 4 * c8 + q, max_units - 1)];
     } else {
-      const int u = min(tt / key_block, max_units - 1);
-      const int id = ids[u];
-      const int jj = id * key_block + (tt - u * key_block);
-      ok = tt < total && id >= 0 && jj <= i;
-      j = ok ? jj : i;
-    }
-    return ok;
-  };
-  struct Step {
-    uint4 kf[4];   // key row of token tl, d [32s + 8qb, +8) for s = 0..3
-    uint4 vq[4];   // value row of token 4u + qb, d [8tl, 8tl + 8) for u = 0..3
-    bool okl;      // this lane's key token is valid
-  };
-  auto load_step = [&](int stp, Step& st) {
-    const int g = stp / nch, t0 = (stp - g * nch) << 4;
-    int jl;
-    st.okl = token(t0 + tl, jl);
-    const bf16_t* kr = K + ((size_t)jl * HKV + g) * D + 8 * qb;
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) st.kf[s2] = *reinterpret_cast<const uint4*>(kr + 32 * s2);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int jv;
-      token(t0 + 4 * u + qb, jv);   // padding tokens weigh 0; the row is valid
-      st.vq[u] = *reinterpret_cast<const uint4*>(V + ((size_t)jv * HKV + g) * D + 8 * tl);
+      raw[0] = ids[min(t0 / key_block, max_units - 1)];
+      raw[4] = ids[min((t0 + 16) / key_block, max_units - 1)];
     }
   };
-  auto load_q = [&](int g, uint4 (&qf)[4]) {
-    const bf16_t* qr = Q + ((size_t)i * HQ + G * g + (tl & 3)) * D + 8 * qb;
+  // global byte offsets of the lane's 8 DMA pieces of chunk ch (row i
+  // stands in for padding, negative ids and keys after the query: they
+  // weigh 0), and the chunk's validity bits (bit t: token t is a support
+  // key; uniform)
+  auto rows_of = [&](int ch, const int (&raw)[8], unsigned (&off)[8]) -> unsigned {
+    const int t0 = ch << 5;
+    unsigned valid = 0u;
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) qf[s2] = *reinterpret_cast<const uint4*>(qr + 32 * s2);
+    for (int c8 = 0; c8 < 8; ++c8) {
+      const int rr = 4 * c8 + q, tt = t0 + rr;
+      bool ok;
+      int r;
+      if constexpr (kUnitTokens) {
+        ok = tt < total && raw[c8] >= 0 && raw[c8] <= i;
+        r = raw[c8];
+      } else {
+        const int sg = c8 >> 2, ts = t0 + 16 * sg, id = raw[4 * sg];
+        ok = tt < total && id >= 0 && id <= i / key_block;   // no overflow below
+        r = ok ? id * key_block + (ts - (ts / key_block) * key_block) + (rr - 16 * sg) : i;
+        ok = ok && r <= i;
+      }
+      off[c8] = (unsigned)(ok ? r : i) * kRowBytes + ((c8 & 1) ? xo1 : xo0);
+      const unsigned long long b = __ballot(ok);   // lanes 0, 16, 32, 48: rows 4c .. 4c+3
+      const unsigned bits = (unsigned)(b & 1ull) | (unsigned)((b >> 15) & 2ull) |
+                            (unsigned)((b >> 30) & 4ull) | (unsigned)((b >> 45) & 8ull);
+      valid |= bits << (4 * c8);
+    }
+    return valid;
+  };
+  auto issue = [&](const unsigned (&off)[8]) {
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) {
+      __builtin_amdgcn_global_load_lds(Kb + off[c8], (lds_ptr_t)(kbuf + 1024 * c8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vb + off[c8], (lds_ptr_t)(vbuf + 1024 * c8), 16, 0, 0);
+    }
   };
 
-  uint4 qf[4];
-  float acc[G][8], m[G], lp[G];
-  const int steps = HKV * nch;
-  // one (KV head, chunk) step on loaded data
-  auto run_step = [&](int stp, const Step& cur) {
-    const int g = stp / nch, ch = stp - g * nch;
-    if (ch == 0) {
-      load_q(g, qf);
+  // query fragment: B operand column n = head n%4, d 32s + 8q + [0, 8)
+  u32x4 qf[4];
+  {
+    const bf16_t* qr = Q + ((size_t)i * HQ + G * g + (lane & 3)) * D + 8 * q;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        m[h] = kNegBig;
-        lp[h] = 0.f;
-      }
-    }
-    // logits of the 4 heads for the chunk's 16 tokens
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[s2]),
-                                                   __builtin_bit_cast(bf16x8, cur.kf[s2]), sc, 0, 0, 0);
-    float p[G], alpha[G];
-    bool moved = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float x = cur.okl ? __fmul_rn(sc[h], c) : -INFINITY;
-      const float mnew = fmaxf(m[h], row16_max(x));
-      alpha[h] = m[h] == mnew ? 1.0f : fast_exp2(m[h] - mnew);
-      moved |= m[h] != mnew;
-      // the running maximum weighs exactly 1 (exp2 of 0 is only ~1 ulp exact)
-      p[h] = !cur.okl ? 0.f : (x == mnew ? 1.0f : fast_exp2(x - mnew));
-      m[h] = mnew;
-    }
-    if (moved) {   // uniform: the row maxima are the same in every lane
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-        lp[h] *= alpha[h];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) lp[h] += p[h];
-    if (lane < 16) pbuf[wave][tl] = make_float4(p[0], p[1], p[2], p[3]);
-    __builtin_amdgcn_wave_barrier();
-    float4 pt[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) pt[u] = pbuf[wave][4 * u + qb];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned w4[4] = {cur.vq[u].x, cur.vq[u].y, cur.vq[u].z, cur.vq[u].w};
-      const float pw[4] = {pt[u].x, pt[u].y, pt[u].z, pt[u].w};
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const float v0 = __uint_as_float(w4[k2] << 16), v1 = __uint_as_float(w4[k2] & 0xffff0000u);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][2 * k2] = fmaf(pw[h], v0, acc[h][2 * k2]);
-          acc[h][2 * k2 + 1] = fmaf(pw[h], v1, acc[h][2 * k2 + 1]);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (ch == nch - 1) {   // head group g done: sum the 4 row groups' tokens
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float l = row16_sum(lp[h]);   // the 16 lanes of a row hold one token each
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = acc[h][e];
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          o[e] = v * inv;
-        }
-        if (qb == 0) {
-          float4* op = reinterpret_cast<float4*>(O + ((size_t)i * HQ + G * g + h) * D + 8 * tl);
-          op[0] = make_float4(o[0], o[1], o[2], o[3]);
-          op[1] = make_float4(o[4], o[5], o[6], o[7]);
-        }
-        if (lse_out && lane == 0)
-          lse_out[(size_t)(G * g + h) * n + i] = l > 0.f ? (m[h] + log2f(l)) * kLn2 : -INFINITY;
-      }
-    }
-  };
-  // two step buffers in turn: the next step's loads are in flight meanwhile
-  Step sa, sb;
-  load_step(0, sa);
-  for (int stp = 0; stp < steps; stp += 2) {
-    if (stp + 1 < steps) load_step(stp + 1, sb);
-    run_step(stp, sa);
-    if (stp + 1 >= steps) break;
-    if (stp + 2 < steps) load_step(stp + 2, sa);
-    run_step(stp + 1, sb);
+    for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qr + 32 * s);
   }
+  // LDS read addresses. Keys: row 16 sigma + m, d-chunk q + 4s at position
+  // (q + 4s) ^ 2(m & 7). Values: lane 16q + 4e + b reads row 4q + e of a
+  // set, d 16 blk + 4b + [0, 4): d-chunk 2 blk + b/2 at position
+  // (2 blk + b/2) ^ 2((4q + e) & 7).
+  uint32_t ka[4], va[8];
+  {
+    const uint32_t kb0 = lds_addr(kbuf) + 256u * m + 16u * (unsigned)(q ^ (2 * (m & 1))) +
+                         64u * (unsigned)((m & 7) >> 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ka[s] = kb0 ^ (64u * s);
+    const int r0 = 4 * q + ((lane >> 2) & 3), b = lane & 3;
+    const uint32_t vb0 = lds_addr(vbuf) + 256u * r0 + 32u * (unsigned)(r0 & 7) + 16u * (b >> 1) + 8u * (b & 1);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) va[blk] = vb0 ^ (32u * blk);
+  }
+  const float lo_sel = (m >= 4 && m < 8) ? 1.0f : 0.0f;   // A-operand rows 4-7 carry lo
+
+  int raw[8];
+  unsigned off[8];
+  fetch_ids(0, raw);
+  unsigned valid_next = rows_of(0, raw, off);
+  issue(off);
+  if (nch > 1) fetch_ids(1, raw);
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = kNegBig, lrun = 0.f;
+  for (int ch = 0; ch < nch; ++ch) {
+    const unsigned valid = valid_next;
+    // every load in flight belongs to this chunk
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    u32x4 kf[8];
+    u32x2 vt[16];
+    read_chunk(ka, va, kf, vt);
+    if (ch + 1 < nch) {   // the buffers are free again: start the next chunk
+      valid_next = rows_of(ch + 1, raw, off);
+      issue(off);
+      if (ch + 2 < nch) fetch_ids(ch + 2, raw);
+    }
+    f32x4 sc[2];
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      sc[sg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[4 * sg + s]),
+                                                         __builtin_bit_cast(bf16x8, qf[s]), sc[sg], 0, 0, 0);
+    }
+    float x[8];   // index 4 sigma + r: token 16 sigma + 4q + r, head lane%4
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3];
+    if (valid != 0xffffffffu) {
+      const unsigned vq = valid >> (4 * q);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((vq >> ((e >> 2) * 16 + (e & 3))) & 1u)) x[e] = -INFINITY;
+    }
+    float smax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+    const float mnew = fmaxf(mrun, smax * c);
+    if (__ballot(mnew != mrun)) {   // a head's maximum moved: rescale
+      const float alpha = mnew == mrun ? 1.0f : fast_exp2(mrun - mnew);
+      lrun *= alpha;
+      const float a0 = quad_bcast<0>(alpha), a1 = quad_bcast<1>(alpha);
+      const float a2 = quad_bcast<2>(alpha), a3 = quad_bcast<3>(alpha);
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+        acc[bb][0] *= a0;
+        acc[bb][1] *= a1;
+        acc[bb][2] *= a2;
+        acc[bb][3] *= a3;
+      }
+      mrun = mnew;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[e], c, -mnew));
+    lrun += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    // A operand: this lane's weights as bf16, hi or lo by its row
+    u32x4 pa;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned hi =
+          __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{p[2 * j], p[2 * j + 1]}, bf16x2));
+      const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+      const f32x2 r2 = {fmaf(-lo_sel, h0, p[2 * j]), fmaf(-lo_sel, h1, p[2 * j + 1])};
+      pa[j] = __builtin_bit_cast(unsigned, __builtin_convertvector(r2, bf16x2));
+    }
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const u32x4 vv = {vt[2 * bb].x, vt[2 * bb].y, vt[2 * bb + 1].x, vt[2 * bb + 1].y};
+      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                        __builtin_bit_cast(bf16x8, vv), acc[bb], 0, 0, 0);
+    }
+  }
+  float l = lrun + __shfl_xor(lrun, 16, 64);   // every lane: head lane%4
+  l += __shfl_xor(l, 32, 64);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float i0 = quad_bcast<0>(inv), i1 = quad_bcast<1>(inv);
+  const float i2 = quad_bcast<2>(inv), i3 = quad_bcast<3>(inv);
+  // result row 4q + r: q = 0 hi, q = 1 lo of head r. Lanes of group 0
+  // write heads 0, 1 and lanes of group 1 heads 2, 3 (d = 16 blk + m).
+  const bool upper = q == 1;
+  float* orow = O + ((size_t)i * HQ + G * g + (upper ? 2 : 0)) * D + m;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    f32x4 t = acc[bb];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], 16, 64);
+    if (q < 2) {
+      orow[16 * bb] = upper ? t[2] * i2 : t[0] * i0;
+      orow[D + 16 * bb] = upper ? t[3] * i3 : t[1] * i1;
+    }
+  }
+  if (lse_out && lane < 4)
+    lse_out[(size_t)(G * g + lane) * n + i] = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int E, int G>
@@ -621,9 +717,8 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
                               hipStream_t stream) {
   if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32 &&
       (key_block == 1 || key_block % 16 == 0)) {
-    const int blocks = (s.n + kMfmaWaves - 1) / kMfmaWaves;
     auto kern = key_block == 1 ? sparse_attn_mfma_kernel<true> : sparse_attn_mfma_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kMfmaWaves), 0, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)s.n * 8u), dim3(64), 0, stream,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                        static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, key_block,
                        max_units, s.scale * kLog2e);
