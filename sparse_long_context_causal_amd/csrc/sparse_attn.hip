@@ -478,53 +478,55 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   // d-chunk m ^ 2((4c + q) & 7): byte offset in the row by the parity of c
   const unsigned xo0 = 16u * (unsigned)(m ^ (2 * q)), xo1 = 16u * (unsigned)(m ^ (8 + 2 * q));
 
-  // Raw token ids of chunk ch for the lane's DMA rows 4c + q (single
-  // tokens), or the block ids of the chunk's two sets (key blocks: a set
-  // never straddles two blocks; raw[0] and raw[4])
-  auto fetch_ids = [&](int ch, int (&raw)[8]) {
+  // Raw token ids of chunk ch: raw[c] for the lane's DMA rows 4c + q and
+  // raw[8] for token lane%32 (single tokens), or the block ids of the
+  // chunk's two sets in raw[0] and raw[4] (key blocks: a set never
+  // straddles two blocks)
+  auto fetch_ids = [&](int ch, int (&raw)[9]) {
     const int t0 = ch << 5;
     if constexpr (kUnitTokens) {
 #pragma unroll
       for (int c8 = 0; c8 < 8; ++c8) raw[c8] = ids[min(t0 + 4 * c8 + q, max_units - 1)];
+      raw[8] = ids[min(t0 + (lane & 31), max_units - 1)];
     } else {
       raw[0] = ids[min(t0 / key_block, max_units - 1)];
       raw[4] = ids[min((t0 + 16) / key_block, max_units - 1)];
     }
   };
-  // global byte offsets of the lane's 8 DMA pieces of chunk ch (row i
-  // stands in for padding, negative ids and keys after the query: they
-  // weigh 0), and the chunk's validity bits (bit t: token t is a support
-  // key; uniform)
-  auto rows_of = [&](int ch, const int (&raw)[8], unsigned (&off)[8]) -> unsigned {
+  // key/value row of token rr of the chunk starting at t0, given its raw id
+  // (single tokens) or its set's block id; false for padding, negative ids
+  // and keys after the query (row i then stands in: it weighs 0)
+  auto token_row = [&](int t0, int rr, int id, int& r) -> bool {
+    if constexpr (kUnitTokens) {
+      r = id;
+      return (t0 + rr < total) & (id >= 0) & (id <= i);
+    } else {
+      const int ts = t0 + (rr & 16);
+      bool ok = (t0 + rr < total) & (id >= 0) & (id <= i / key_block);   // no overflow below
+      r = ok ? id * key_block + (ts - (ts / key_block) * key_block) + (rr & 15) : i;
+      return ok & (r <= i);
+    }
+  };
+  // global byte offsets of the lane's 8 DMA pieces of chunk ch, and the
+  // chunk's validity bits (bit t: token t is a support key; uniform)
+  auto rows_of = [&](int ch, const int (&raw)[9], unsigned (&off)[8]) -> unsigned {
     const int t0 = ch << 5;
-    unsigned valid = 0u;
 #pragma unroll
     for (int c8 = 0; c8 < 8; ++c8) {
-      const int rr = 4 * c8 + q, tt = t0 + rr;
-      bool ok;
       int r;
-      if constexpr (kUnitTokens) {
-        ok = tt < total && raw[c8] >= 0 && raw[c8] <= i;
-        r = raw[c8];
-      } else {
-        const int sg = c8 >> 2, ts = t0 + 16 * sg, id = raw[4 * sg];
-        ok = tt < total && id >= 0 && id <= i / key_block;   // no overflow below
-        r = ok ? id * key_block + (ts - (ts / key_block) * key_block) + (rr - 16 * sg) : i;
-        ok = ok && r <= i;
-      }
+      const bool ok = token_row(t0, 4 * c8 + q, kUnitTokens ? raw[c8] : raw[4 * (c8 >> 2)], r);
       off[c8] = (unsigned)(ok ? r : i) * kRowBytes + ((c8 & 1) ? xo1 : xo0);
-      const unsigned long long b = __ballot(ok);   // lanes 0, 16, 32, 48: rows 4c .. 4c+3
-      const unsigned bits = (unsigned)(b & 1ull) | (unsigned)((b >> 15) & 2ull) |
-                            (unsigned)((b >> 30) & 4ull) | (unsigned)((b >> 45) & 8ull);
-      valid |= bits << (4 * c8);
     }
-    return valid;
+    int r;
+    const bool okt = token_row(t0, lane & 31, kUnitTokens ? raw[8] : ((lane & 16) ? raw[4] : raw[0]), r);
+    return (unsigned)__ballot(okt);   // lanes 0..31: tokens 0..31
   };
+  const uint32_t kb_lds = lds_addr(kbuf), vb_lds = lds_addr(vbuf);
   auto issue = [&](const unsigned (&off)[8]) {
 #pragma unroll
     for (int c8 = 0; c8 < 8; ++c8) {
-      __builtin_amdgcn_global_load_lds(Kb + off[c8], (lds_ptr_t)(kbuf + 1024 * c8), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vb + off[c8], (lds_ptr_t)(vbuf + 1024 * c8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Kb + off[c8], (lds_ptr_t)(uintptr_t)(kb_lds + 1024u * c8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vb + off[c8], (lds_ptr_t)(uintptr_t)(vb_lds + 1024u * c8), 16, 0, 0);
     }
   };
 
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   }
   const float lo_sel = (m >= 4 && m < 8) ? 1.0f : 0.0f;   // A-operand rows 4-7 carry lo
 
-  int raw[8];
+  int raw[9];
   unsigned off[8];
   fetch_ids(0, raw);
   unsigned valid_next = rows_of(0, raw, off);
