@@ -6,15 +6,18 @@
 // (token ids, or 64-token key blocks from the indexer); the softmax is taken
 // over the support only. The abstract states the same recompute step.
 //
-// One wavefront per query row, rows issued longest first. All Hq heads share
-// the row's support, so one gathered token row K[j] (all Hkv heads, d
-// contiguous: Hkv*d elements) serves every head: lane l holds a contiguous
-// slice of E = Hkv*d/64 elements of that row, i.e. a d-slice of KV head
-// g = l / (d/E). The lane keeps its G query heads' slices of Q and of the
-// output in registers; logits are lane partial dot products summed over the
-// d/E lanes of the group with xor shuffles. Tokens are processed in chunks:
-// loads for a chunk are issued together, then one online-softmax rescale per
-// chunk, then P*V in fp32 (no rounding of P).
+// Three kernels. bf16 with d = 128 and 8 KV heads x 4 query heads runs on
+// MFMAs (sparse_attn_mfma_kernel, at the end of this file). The other
+// shapes use one wavefront per query row, rows issued longest first: all Hq
+// heads share the row's support, so one gathered token row K[j] (all Hkv
+// heads, d contiguous: Hkv*d elements) serves every head. In the generic
+// kernel lane l holds a contiguous slice of E = Hkv*d/64 elements of that
+// row, i.e. a d-slice of KV head g = l / (d/E); it keeps its G query heads'
+// slices of Q and of the output in registers, and logits are lane partial
+// dot products summed over the d/E lanes of the group with xor shuffles.
+// Tokens are processed in chunks: loads for a chunk are issued together,
+// then one online-softmax rescale per chunk, then P*V in fp32 (no rounding
+// of P).
 #include "device_common.h"
 #include "kernels.h"
 
