@@ -331,6 +331,29 @@ __device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* words,
   rs.btau[r] = bt;
 }
 
+// The same for a row whose state the caller already holds (cnt = candidates
+// appended so far; seen, cge and bt as stored): the histogram words of the
+// next 8 bins come in one batch of reads, as the bound rarely moves further.
+__device__ __forceinline__ void raise_bound_from(RowState& rs, const unsigned* words, int r,
+                                                 int budget, int cnt, int seen, int cge, int bt) {
+  int cg = cge + (cnt - seen);
+  const int w0 = bt >> 1;
+  unsigned wv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wv[j] = words[min(w0 + j, kFBinWords - 1)];
+  while (bt < kFBins - 1) {
+    const int j = (bt >> 1) - w0;
+    const unsigned w = j == 0 ? wv[0] : j == 1 ? wv[1] : j == 2 ? wv[2] : j == 3 ? wv[3] : words[bt >> 1];
+    const int hb = (int)((w >> ((bt & 1) * 16)) & 0xffffu);
+    if (cg - hb < budget) break;
+    cg -= hb;
+    ++bt;
+  }
+  rs.seen[r] = cnt;
+  rs.cge[r] = cg;
+  rs.btau[r] = bt;
+}
+
 // Swizzled partial-mass layout: element (register r, source lane) of KV head
 // g's tile lives at word r*64 + (lane ^ 4r) of that head's 4 KiB block, so
 // both the lane-major writes and the row-owner reads are bank-conflict free.
@@ -340,12 +363,13 @@ __device__ __forceinline__ int part_index(int g, int r, int src_lane) {
   return (g * 16 + r) * 64 + (src_lane ^ (4 * r));
 }
 
-template <typename T, int D, int G, int KB>
+template <typename T, int D, int G, int KB, int HK>   // HK: the KV heads if fixed at 8, else 0
 __global__ __launch_bounds__(512) void pass2_filter_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ lse, int n,
-    int hkv, float c, float inv_hq, int budget, uint2* __restrict__ cand, int cap,
+    int hkv_arg, float c, float inv_hq, int budget, uint2* __restrict__ cand, int cap,
     int* __restrict__ cand_count, int* __restrict__ row_bin, int* __restrict__ ovf_count,
     int* __restrict__ ovf_list) {
+  const int hkv = HK ? HK : hkv_arg;
   typedef KTile<T, D> KT;
   constexpr int NC = KT::kChunks;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -483,25 +507,41 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       // the bin's floor pattern, so the bin itself is only formed for the
       // histogram of appended entries.
       const int bt = rs.btau[own_n];
+      const int pos0 = rs.cnt[own_n];
+      const int seen = rs.seen[own_n], cge = rs.cge[own_n];
       const unsigned thr = filter_bin_floor_bits(bt);
-      int pos = rs.cnt[own_n];
+      int pos = pos0;
       const bool live = own_ok && pos <= cap;
       // Lane j of a row's lane group takes the row's keys k0 + m with
       // m = e*lpq + j, so each ballot round appends in increasing key order
       // and, tile after tile, every row's pool is sorted by key. Key offset m
       // sits in accumulator register r = 4*(m/8) + m%4 of lane half (m/4)%2.
-      for (int e = 0; e < epl; ++e) {
+      // mass of the lane's key offset e*lpq + own_j, summed over the KV
+      // heads in a fixed order
+      auto mass = [&](int e) -> float {
         const int mo = e * lpq + own_j;
         const int r = ((mo >> 3) << 2) | (mo & 3), h2 = (mo >> 2) & 1;
         const float* src = pb + part_index(0, r, own_n + 32 * h2);
-        float p = src[0];   // summed over KV heads in a fixed order
-        if (hkv == 8) {
+        float p = src[0];
+        if constexpr (HK == 8) {
 #pragma unroll
           for (int gg = 1; gg < 8; ++gg) p += src[gg * 16 * 64];
         } else {
           for (int gg = 1; gg < hkv; ++gg) p += src[gg * 16 * 64];
         }
-        p *= inv_hq;
+        return p * inv_hq;
+      };
+      // with the KV heads fixed at 8 both masses are read in one batch first
+      float pm[2];
+      if constexpr (HK == 8) {
+        pm[0] = mass(0);
+        pm[1] = mass(1);
+      }
+      for (int e = 0; e < epl; ++e) {
+        const int mo = e * lpq + own_j;
+        float p;
+        if constexpr (HK == 8) p = pm[e];
+        else p = mass(e);
         const unsigned bits = __float_as_uint(p);
         const int key = k0 + mo;
         const bool flag = own_ok && bits >= thr && (!diag || key <= own_q);
@@ -516,9 +556,11 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         }
         pos += __popcll(m);
       }
-      if (own_j == 0 && own_ok) {
+      // the bound can only rise after appends (the histogram is unchanged
+      // otherwise)
+      if (own_j == 0 && own_ok && pos != pos0) {
         rs.cnt[own_n] = pos;
-        if (pos <= cap) raise_bound(rs, own_hist, own_n, budget);
+        if (pos <= cap) raise_bound_from(rs, own_hist, own_n, budget, pos, seen, cge, bt);
       }
     } else {
       // ---- key blocks of KB = 64 tokens = two key tiles
@@ -595,7 +637,7 @@ static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, cons
                             const float* lse, const CandidatePool& pool, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
   const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB);
-  auto kern = pass2_filter_kernel<T, D, G, KB>;
+  auto kern = s.hkv == 8 ? pass2_filter_kernel<T, D, G, KB, 8> : pass2_filter_kernel<T, D, G, KB, 0>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
