@@ -122,6 +122,8 @@ int topk_support_stage(const amtk_attn_desc* attn, const amtk_support_desc* sup,
  * key block ids, expanded to tokens b*64 .. b*64+63 and clipped to j <= i.
  * Negative ids and tokens j > i are skipped; count[i] is clamped to
  * [0, max_units]. A row with an empty support gets O = 0 and LSE = -inf.
+ * The ids of a row may come in any order; they are expected to be distinct
+ * (topk_support writes them so), a repeated id counting once per entry.
  *
  * idx       : [n][max_units] int32 (device); count: [n] int32 (device).
  * o         : OUT [n][hq][d] fp32.

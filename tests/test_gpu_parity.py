@@ -257,6 +257,49 @@ def test_sparse_attn_one_token_and_empty(gpu_lib):
             np.testing.assert_array_equal(out[i, h], x["v"][i // 2, h // 4])
 
 
+@pytest.mark.parametrize("key_block", [1, 64])
+def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block):
+    """The MFMA path (bf16, d=128, 32/8 heads) on hand-made supports: ids in
+    random order (the running maximum moves late), negative ids and ids past
+    the row mixed in, counts above max_units (clamped), empty rows. Every row
+    is checked against the oracle on the ids the contract keeps."""
+    import torch
+    amtk = gpu_lib
+    n, max_units = 300, 48
+    rng = np.random.default_rng(77 + key_block)
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=43, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    idx = np.full((n, max_units), -1, dtype=np.int32)
+    cnt = np.zeros(n, dtype=np.int32)
+    for i in range(n):
+        top = i if key_block == 1 else i // key_block
+        m = int(rng.integers(0, max_units + 12))          # up to 11 past max_units
+        ids = rng.permutation(top + 1)[: max(0, m - 3)].tolist()
+        ids += [-1, top + 1 + int(rng.integers(0, 5)), -7][: m - len(ids)]
+        ids = rng.permutation(np.asarray(ids, dtype=np.int64)).tolist() if ids else []
+        idx[i, : min(len(ids), max_units)] = ids[:max_units]
+        cnt[i] = m
+    cnt[7] = 0
+    cnt[150] = 0
+    d = upload(x, "bf16")
+    out, lse = amtk.sparse_attn(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
+                                torch.from_numpy(cnt).cuda(), key_block, want_lse=True)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in range(n):
+        kept = [int(u) for u in idx[i, : min(int(cnt[i]), max_units)] if u >= 0]
+        if key_block == 1:
+            toks = [j for j in kept if j <= i]
+        else:
+            toks = [j for b in kept for j in range(b * 64, b * 64 + 64) if j <= i]
+        if not toks:
+            assert np.all(out[i] == 0) and np.all(np.isneginf(lse[:, i])), f"row {i}"
+            continue
+        o_ref, l_ref = layer.attention_on(i, toks)
+        err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
+        assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
+        assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
+
+
 # ------------------------------------------------------------ the workloads
 def _workload_check(amtk, name, rows_cap=None, n=None):
     w = WORKLOADS[name]
