@@ -174,6 +174,12 @@ def causal_sparsity(n: int, k: int) -> float:
     return float(1.0 - kept / ((n * (n + 1)) / 2.0))
 
 
+def query_block_rows(t: int, b_sel: int, n: int) -> range:
+    """Query rows of selection block t: b_sel consecutive rows, the last block
+    holding what is left of [0, N)."""
+    return range(t * b_sel, min((t + 1) * b_sel, n))
+
+
 class OracleLayer:
     """The oracle for one GQA layer: per-row support selection and outputs.
 
@@ -217,6 +223,42 @@ class OracleLayer:
         if dense:
             res["dense_out"] = dense_attention(s, lse, self.v_t, i)
         return res
+
+    def query_block(self, t: int, k: int, b_sel: int = 64) -> dict:
+        """Support shared by selection block t (b_sel consecutive query rows).
+
+        [TB 2.1]: with selection-block-shared granularity (b_sel = 64) one
+        support set is chosen for a block of consecutive queries, to amortise
+        system costs. READING: the block scores key j by the mean over its
+        rows of their head-averaged masses P_i(j), a key after row i counting
+        0 for that row; the top-k keys by (score descending, id ascending)
+        among the keys the block's last row sees are shared by every row of
+        the block; each row then attends over the shared keys j <= i.
+
+        Keys: rows; score [last row + 1]; units (ascending); unit_mass; kth;
+        out {i: [Hq,d]} and lse_s {i: [Hq]} per row (zeros and -inf for a
+        row that sees none of the shared keys).
+        """
+        rows = query_block_rows(t, b_sel, self.n)
+        last = rows[-1]
+        score = np.zeros(last + 1, dtype=np.float64)
+        logits = {}
+        for i in rows:
+            s = self.logits(i)
+            score[: i + 1] += head_mass(s, log_sum_exp(s))
+            logits[i] = s
+        score /= len(rows)
+        units = top_units(score, k)
+        out, lse_s = {}, {}
+        for i in rows:
+            sup = units[units <= i]
+            if sup.size:
+                out[i], lse_s[i] = support_attention(logits[i], self.v_t, sup)
+            else:
+                out[i] = np.zeros((self.hq, self.d))
+                lse_s[i] = np.full(self.hq, -math.inf)
+        return {"rows": rows, "score": score, "units": units, "unit_mass": score[units],
+                "kth": kth_score(score, k), "out": out, "lse_s": lse_s}
 
     def attention_on(self, i: int, support: Sequence[int]):
         """Sparse output of row i on a given support (used with the GPU's support)."""

@@ -41,3 +41,13 @@ def full_sparse_out(logits, v, supports):
     lg = np.where(mask[None], logits, -np.inf)
     w = softmax(lg, axis=-1)
     return np.einsum("hij,jhc->ihc", w, v_rep)
+
+
+def full_block_topk(P, rows, k):
+    """Shared top-k of a block of query rows from the full mass matrix: the
+    column mean over the rows (entries past a row's diagonal are 0 in P),
+    ranked by one stable argsort over the keys the last row sees."""
+    last = rows[-1]
+    score = P[list(rows), : last + 1].mean(axis=0)
+    order = np.argsort(-score, kind="stable")
+    return score, np.sort(order[: min(k, last + 1)])

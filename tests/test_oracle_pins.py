@@ -108,6 +108,70 @@ def test_against_brute_force(shape, kk):
         np.testing.assert_allclose(layer.row(i, kk)["out"], o_bf[i], atol=1e-12)
 
 
+@pytest.mark.parametrize("shape,b_sel", [((70, 8, 2, 16), 16), ((45, 4, 1, 8), 64),
+                                         ((64, 6, 3, 32), 8)])
+@pytest.mark.parametrize("kk", [1, 6, 20])
+def test_query_blocks_against_brute_force(shape, b_sel, kk):
+    """Selection-block-shared support: block scores, shared top-k and every
+    row's output against the full-tensor formulation (masked softmax, mean
+    over heads, column mean over the block's rows, stable argsort)."""
+    n, hq, hkv, d = shape
+    x = random_inputs(n, hq, hkv, d, "f32", seed=11 * n + kk + b_sel, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    P, probs, logits = bf.full_mass(x["q"], x["k"], 1 / math.sqrt(d))
+    supports = []
+    for t in range((n + b_sel - 1) // b_sel):
+        r = layer.query_block(t, kk, b_sel)
+        rows = list(r["rows"])
+        assert rows == list(range(t * b_sel, min(n, (t + 1) * b_sel)))
+        score, units = bf.full_block_topk(P, rows, kk)
+        np.testing.assert_allclose(r["score"], score, atol=1e-12, rtol=0)
+        assert abs(r["score"].sum() - 1) < 1e-12
+        assert r["units"].tolist() == units.tolist()
+        for i in rows:
+            supports.append(units[units <= i])
+    o_bf = bf.full_sparse_out(logits, x["v"], supports)
+    for t in range((n + b_sel - 1) // b_sel):
+        r = layer.query_block(t, kk, b_sel)
+        for i in r["rows"]:
+            np.testing.assert_allclose(r["out"][i], o_bf[i], atol=1e-12)
+
+
+def test_query_block_of_one_row_is_per_query_and_full_budget_is_dense():
+    n, hq, hkv, d = 40, 4, 2, 16
+    x = random_inputs(n, hq, hkv, d, "f32", seed=5, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in range(n):
+        a, b = layer.query_block(i, 7, 1), layer.row(i, 7)
+        assert a["units"].tolist() == b["units"].tolist()
+        np.testing.assert_array_equal(a["score"], b["p"])
+        np.testing.assert_array_equal(a["out"][i], b["out"])
+    # a budget covering the block's last row keeps every key: each row's
+    # output is then its dense attention
+    for t in range(3):
+        r = layer.query_block(t, n, 16)
+        assert r["units"].tolist() == list(range(r["rows"][-1] + 1))
+        for i in r["rows"]:
+            np.testing.assert_allclose(r["out"][i], layer.dense(i), atol=1e-12)
+
+
+def test_query_block_equal_keys_closed_form():
+    """All keys equal: row i spreads 1/(i+1) over keys 0..i, so the block
+    score of key j is the mean over the block's rows i >= j of 1/(i+1)
+    (keys after a row count 0 for it), and ties go to the smallest ids."""
+    n, hq, hkv, d, b_sel = 50, 4, 2, 8, 16
+    x = random_inputs(n, hq, hkv, d, "f32", seed=9)
+    x["k"][:] = x["k"][0]
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for t in range(4):
+        r = layer.query_block(t, 5, b_sel)
+        rows = list(r["rows"])
+        want = np.array([sum(1.0 / (i + 1) for i in rows if i >= j) / len(rows)
+                         for j in range(rows[-1] + 1)])
+        np.testing.assert_allclose(r["score"], want, rtol=1e-12, atol=0)
+        assert r["units"].tolist() == list(range(5))
+
+
 def test_dense_against_torch_sdpa():
     n, hq, hkv, d = 64, 8, 2, 32
     x = random_inputs(n, hq, hkv, d, "f32", seed=3, sink=True)
