@@ -44,16 +44,18 @@ def source_hash(rel):
     return h.hexdigest()[:16]
 
 
-def support_tokens(plan, key_block):
+def support_tokens(plan, key_block, query_block=1):
     """Tokens gathered by sparse_attn: sum over rows of the selected units' visible keys."""
     import torch
     cnt = plan.count.to(torch.int64)
-    if key_block == 1:
+    if key_block == 1 and query_block == 1:
         return int(cnt.sum().item())
     n, kk = plan.idx.shape
     rows = torch.arange(n, device=plan.idx.device, dtype=torch.int64)[:, None]
     b = plan.idx.to(torch.int64)
     valid = (torch.arange(kk, device=b.device)[None, :] < cnt[:, None]) & (b >= 0)
+    if key_block == 1:      # a shared support: each row gathers its ids up to itself
+        return int((valid & (b <= rows)).sum().item())
     toks = torch.clamp(rows + 1 - b * key_block, min=0, max=key_block)
     return int(torch.where(valid, toks, torch.zeros_like(toks)).sum().item())
 
@@ -82,7 +84,7 @@ def traffic_for(kernel, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, k, key_block, budget_s=25.0):
+def cpu_baseline(w, x, k, key_block, budget_s=25.0, query_block=1):
     """The fp64 oracle on a seeded row sample of the same layer, extrapolated by row length."""
     import numpy as np
     from oracle import OracleLayer, IndexerOracle
@@ -93,6 +95,8 @@ def cpu_baseline(w, x, k, key_block, budget_s=25.0):
     except Exception:
         threads = 1
     n = x["q"].shape[0]
+    if query_block > 1:
+        return _cpu_baseline_blocks(w, x, k, query_block, budget_s, threads)
     # a seeded uniform row sample, visited in seeded random order until the
     # time budget is spent (so any prefix of it is itself a uniform sample)
     rows = sample_rows(w, n=n, count=min(n, 4096))
@@ -120,6 +124,31 @@ def cpu_baseline(w, x, k, key_block, budget_s=25.0):
             "ms_per_row": 1000.0 * t_rows / max(done.size, 1)}
 
 
+def _cpu_baseline_blocks(w, x, k, b_sel, budget_s, threads):
+    """The oracle's selection-block path on seeded blocks, extrapolated by the
+    blocks' summed row lengths."""
+    import numpy as np
+    from oracle import OracleLayer, query_block_rows
+    n = x["q"].shape[0]
+    nblk = (n + b_sel - 1) // b_sel
+    order = np.random.default_rng(w.row_seed + 2).permutation(nblk)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    done, cost, t_all = 0, 0.0, 0.0
+    for t in order:
+        t0 = time.perf_counter()
+        layer.query_block(int(t), k, b_sel)
+        t_all += time.perf_counter() - t0
+        done += 1
+        cost += sum(i + 1 for i in query_block_rows(int(t), b_sel, n))
+        if t_all > budget_s:
+            break
+    full_s = t_all * (n * (n + 1) / 2.0) / cost
+    return {"value": n / full_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{done} seeded selection blocks of {b_sel} rows (of {nblk}) of {w.name}, "
+                       f"full fp64 oracle per block ({t_all:.1f} s), layer time extrapolated by "
+                       f"row length (cost ~ i+1): {full_s:.1f} s")}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +156,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_bf16_32k")
     ap.add_argument("--k", type=int, default=None, help="budget (default: the workload's)")
+    ap.add_argument("--query-block", type=int, default=1, choices=(1, 64),
+                    help="1: a support per query; 64: one support per block of 64 queries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -166,10 +197,16 @@ def main():
     if w.indexer_d:
         extra = {key: torch.from_numpy(x[key]).to(torch.bfloat16).to(dev)
                  for key in ("q_idx", "k_idx")}
-    plan = amtk.PrefillPlan(t["q"], t["k"], t["v"], k, w.key_block, **extra)
+    qb = args.query_block
+    if qb != 1 and (w.indexer_d or w.key_block != 1):
+        print("bench.py: --query-block 64 applies to the oracle path with key_block 1",
+              file=sys.stderr)
+        sys.exit(2)
+    plan = amtk.PrefillPlan(t["q"], t["k"], t["v"], k, w.key_block, query_block=qb, **extra)
     stream = torch.cuda.current_stream(dev)
     names = ["indexer_topk", "sparse_attn"] if w.indexer_d else \
-        ["pass1_lse", "pass2_filter", "select", "sparse_attn"]
+        ["pass1_lse", "pass2_filter", "select", "sparse_attn"] if qb == 1 else \
+        ["pass1_lse", "pass2_colsum", "block_topk", "sparse_attn"]
     pieces = [plan.indexer_call, plan.attn] if w.indexer_d else \
         [lambda: plan.stage(1), lambda: plan.stage(2), lambda: plan.stage(3), plan.attn]
 
@@ -196,7 +233,7 @@ def main():
         + ", ".join(f"{k_}={v:.3f}" for k_, v in per.items()))
 
     n = w.n
-    sup = support_tokens(plan, w.key_block)
+    sup = support_tokens(plan, w.key_block, qb)
     qk_flops, attn_bytes = algorithmic_work(w, n, k, sup)
     peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kernels = {}
@@ -205,8 +242,8 @@ def main():
         kernels["indexer_topk"] = {"bound": "mfma", "work": idx_flops, "ms": per["indexer_topk"]}
     else:
         kernels["pass1_lse"] = {"bound": "mfma", "work": qk_flops, "ms": per["pass1_lse"]}
-        kernels["pass2_filter"] = {"bound": "mfma", "work": qk_flops, "ms": per["pass2_filter"]}
-        kernels["select"] = {"bound": "alu", "work": None, "ms": per["select"]}
+        kernels[names[1]] = {"bound": "mfma", "work": qk_flops, "ms": per[names[1]]}
+        kernels[names[2]] = {"bound": "alu", "work": None, "ms": per[names[2]]}
     kernels["sparse_attn"] = {"bound": "hbm", "work": attn_bytes, "ms": per["sparse_attn"]}
     dom = max((kn for kn in kernels if kernels[kn]["work"]), key=lambda kn: kernels[kn]["ms"])
     kd = kernels[dom]
@@ -219,7 +256,8 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": achieved / peak_mfma}
     roof["kernel"] = dom
-    roof["traffic"] = traffic_for(dom, w.name) if dom in KERNEL_SOURCES else None
+    tkey = w.name if qb == 1 else f"{w.name}_qb{qb}"
+    roof["traffic"] = traffic_for(dom, tkey) if dom in KERNEL_SOURCES else None
 
     summary = {}
     for kn, kv in kernels.items():
@@ -233,13 +271,13 @@ def main():
                 ent["frac_mfma"] = round(ent["TFLOP/s"] / peak_mfma, 4)
         summary[kn] = ent
     if not w.indexer_d:
-        t12 = (per["pass1_lse"] + per["pass2_filter"]) * 1e-3
+        t12 = (per["pass1_lse"] + per[names[1]]) * 1e-3
         summary["passes_1_2_frac_mfma"] = round(2 * qk_flops / t12 / 1e12 / peak_mfma, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline on a row sample ...")
-        cpu = cpu_baseline(w, x, k, w.key_block, args.cpu_seconds)
+        cpu = cpu_baseline(w, x, k, w.key_block, args.cpu_seconds, qb)
         log(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s ({cpu['sample']})")
 
     line = {
@@ -256,7 +294,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) Q/K/V, sink key, planted needle keys)",
         "config": {"workload": w.name, "n": n, "hq": w.hq, "hkv": w.hkv, "d": w.d, "k": k,
-                   "key_block": w.key_block, "support_tokens": sup, "parallelism": "none"},
+                   "key_block": w.key_block, "query_block": qb, "support_tokens": sup,
+                   "parallelism": "none"},
         "roofline": roof,
         "kernels": summary,
         "cpu_baseline": cpu,

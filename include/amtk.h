@@ -60,7 +60,8 @@ typedef struct {
 typedef struct {
   int32_t k;             /* budget, in key_block units, 1 <= k <= 8192 */
   int32_t key_block;     /* 1 = token support, 64 = aligned 64-token key blocks */
-  int32_t query_block;   /* queries sharing one support (b_sel); must be 1 */
+  int32_t query_block;   /* queries sharing one support (b_sel): 1 (per query) or
+                            64 (with key_block = 1), see topk_support */
   int32_t candidate_cap; /* candidates kept per row by the streaming filter;
                             0 = automatic; values above 65000 are clamped.
                             Rows that exceed it are recomputed densely, so
@@ -83,10 +84,20 @@ int amtk_topk_workspace(const amtk_attn_desc* attn, const amtk_support_desc* sup
  * Two passes over the causal score matrix (per-head LSE, then mass + streaming
  * threshold filter) and an exact select; the n x n mass is never stored.
  *
+ * query_block = 64 ([TB 2.1]: a selection-block-shared support, one support
+ * set for a block of 64 consecutive queries): the block scores key j by the
+ * mean over its rows of P_i(j), keys after row i counting 0 for that row, and
+ * its top-k keys among those its last row sees are written into the index
+ * row of every query of the block (mass = the block score). sparse_attn then
+ * skips, for each row, the shared keys after it. The last block holds the
+ * remaining rows. Pass 2 then writes the column sums of P over each 32-row
+ * tile into the workspace ((n+31)/32 x n floats) instead of filtering.
+ *
  * q, k      : inputs as described above.
  * idx       : OUT [n][k] int32, row i's selected unit ids (token ids, or key
  *             block ids when key_block = 64) ascending, then -1 padding.
- * count     : OUT [n] int32, number of selected units = min(k, visible units).
+ * count     : OUT [n] int32, number of selected units = min(k, visible units)
+ *             (query_block = 64: the keys the block's last row sees).
  * mass      : OUT [n][k] fp32 mass of each selected unit (0 padding), or NULL.
  * lse       : OUT [hq][n] fp32 per-head dense log-sum-exp (natural log), or NULL.
  * ws        : device workspace of ws_bytes >= amtk_topk_workspace(); its
@@ -175,6 +186,7 @@ int amtk_last_hip_error(void);
  * counts back and reports the largest count, the number of rows whose pool
  * overflowed the capacity (recomputed densely), and the capacity itself.
  * SYNCHRONOUS: waits for `stream`. For tests and tuning only.
+ * AMTK_E_UNSUPPORTED for query_block = 64 (no candidate pools are kept).
  */
 int amtk_pool_stats(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* ws,
                     size_t ws_bytes, int64_t* max_candidates, int64_t* overflow_rows,

@@ -82,8 +82,9 @@ def attn_desc(q, k, scale: Optional[float] = None) -> AttnDesc:
                     float(scale) if scale else 0.0)
 
 
-def support_desc(budget: int, key_block: int = 1, candidate_cap: int = 0) -> SupportDesc:
-    return SupportDesc(int(budget), int(key_block), 1, int(candidate_cap))
+def support_desc(budget: int, key_block: int = 1, candidate_cap: int = 0,
+                 query_block: int = 1) -> SupportDesc:
+    return SupportDesc(int(budget), int(key_block), int(query_block), int(candidate_cap))
 
 
 def _call(name, *args):
@@ -111,12 +112,13 @@ def workspace(nbytes: int, device):
 
 def topk_support(q, k, budget: int, key_block: int = 1, scale: Optional[float] = None,
                  candidate_cap: int = 0, want_mass: bool = True, want_lse: bool = True,
-                 ws=None):
+                 ws=None, query_block: int = 1):
     """Oracle support selection. Returns (idx [N,k] int32, count [N] int32,
-    mass [N,k] fp32 or None, lse [Hq,N] fp32 or None)."""
+    mass [N,k] fp32 or None, lse [Hq,N] fp32 or None). query_block = 64 shares
+    one support among each block of 64 consecutive queries."""
     torch = _torch()
     _check_dev(q, k)
-    ad, sd = attn_desc(q, k, scale), support_desc(budget, key_block, candidate_cap)
+    ad, sd = attn_desc(q, k, scale), support_desc(budget, key_block, candidate_cap, query_block)
     n, hq = q.shape[0], q.shape[1]
     if ws is None:
         ws = workspace(topk_workspace_bytes(ad, sd), q.device)
@@ -152,13 +154,13 @@ def sparse_attn(q, k, v, idx, count, key_block: int = 1, scale: Optional[float] 
 
 def oracle_prefill(q, k, v, budget: int, key_block: int = 1, scale: Optional[float] = None,
                    candidate_cap: int = 0, want_mass: bool = True, want_lse: bool = True,
-                   ws=None):
+                   ws=None, query_block: int = 1):
     """topk_support + sparse_attn. Returns (out, idx, count, mass, lse)."""
     torch = _torch()
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    ad, sd = attn_desc(q, k, scale), support_desc(budget, key_block, candidate_cap)
+    ad, sd = attn_desc(q, k, scale), support_desc(budget, key_block, candidate_cap, query_block)
     n, hq, d = q.shape
     if ws is None:
         ws = workspace(topk_workspace_bytes(ad, sd), q.device)
@@ -216,7 +218,8 @@ class PrefillPlan:
     topk_support, then sparse_attn over 64-token key blocks.
     """
 
-    def __init__(self, q, k, v, budget, key_block=1, q_idx=None, k_idx=None, candidate_cap=0):
+    def __init__(self, q, k, v, budget, key_block=1, q_idx=None, k_idx=None, candidate_cap=0,
+                 query_block=1):
         torch = _torch()
         _check_dev(q, k, v)
         self.q, self.k, self.v = q, k, v
@@ -224,7 +227,7 @@ class PrefillPlan:
         self.budget, self.key_block = int(budget), int(key_block)
         self.indexer = q_idx is not None
         self.ad = attn_desc(q, k)
-        self.sd = support_desc(budget, key_block, candidate_cap)
+        self.sd = support_desc(budget, key_block, candidate_cap, query_block)
         dev = q.device
         if self.indexer:
             _check_dev(q_idx, k_idx)

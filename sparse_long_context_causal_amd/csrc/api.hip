@@ -24,6 +24,9 @@ thread_local int g_last_hip = 0;
 // counts candidates per mass bin in 16-bit LDS counters.
 constexpr int kMaxCap = 65000;
 
+// Rows per selection block when a support is shared by consecutive queries.
+constexpr int kQueryBlock = 64;
+
 int hip_fail(hipError_t e) {
   g_last_hip = (int)e;
   return AMTK_E_HIP;
@@ -56,18 +59,29 @@ int check_support(const amtk_support_desc* sp) {
   if (sp->k < 1 || sp->candidate_cap < 0) return AMTK_E_INVALID;
   if (sp->k > amtk::kMaxBudget) return AMTK_E_UNSUPPORTED;
   if (sp->key_block != 1 && sp->key_block != 64) return AMTK_E_UNSUPPORTED;
-  if (sp->query_block != 1) return AMTK_E_UNSUPPORTED;
+  if (sp->query_block != 1 && sp->query_block != kQueryBlock) return AMTK_E_UNSUPPORTED;
+  if (sp->query_block == kQueryBlock && sp->key_block != 1) return AMTK_E_UNSUPPORTED;
   return AMTK_OK;
 }
 
 struct Layout {
-  size_t cand, count, bin, lse, ovf_count, ovf_list, scratch, total;
+  size_t cand, count, bin, lse, ovf_count, ovf_list, scratch, colsum, total;
   int cap, units_max;
 };
 
 Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
   Layout L;
   const size_t n = (size_t)s.n;
+  if (sp.query_block != 1) {   // selection blocks: LSE and the tiles' column sums
+    L = Layout{};
+    L.units_max = s.n;
+    size_t off = 0;
+    L.lse = off;     off = round_up(off + (size_t)s.hq * n * sizeof(float));
+    L.ovf_count = off; off = round_up(off + sizeof(int));
+    L.colsum = off;  off = round_up(off + (n + 31) / 32 * n * sizeof(float));
+    L.total = off;
+    return L;
+  }
   L.units_max = sp.key_block == 1 ? s.n : (s.n - 1) / sp.key_block + 1;
   int cap = sp.candidate_cap > 0 ? sp.candidate_cap
                                  : (8 * sp.k > 4096 ? 8 * sp.k : 4096);
@@ -82,6 +96,7 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
   L.ovf_count = off;  off = round_up(off + sizeof(int));
   L.ovf_list = off;   off = round_up(off + n * sizeof(int));
   L.scratch = off;    off = round_up(off + (size_t)amtk::kFallbackSlots * L.units_max * sizeof(float));
+  L.colsum = 0;
   L.total = off;
   return L;
 }
@@ -113,9 +128,19 @@ int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const 
     return AMTK_E_INVALID;
   const Layout L = layout(s, sp);
   if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
-  const CandidatePool pool = pool_of(ws, L);
   float* lse_buf = lse ? lse : reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + L.lse);
   hipError_t e = hipSuccess;
+  if (sp.query_block != 1) {   // one support per selection block of consecutive queries
+    float* colsum = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + L.colsum);
+    int* zero = reinterpret_cast<int*>(static_cast<unsigned char*>(ws) + L.ovf_count);
+    if (stage == 0 || stage == 1) e = amtk::launch_pass1_lse(s, q, k, lse_buf, zero, stream);
+    if (e == hipSuccess && (stage == 0 || stage == 2))
+      e = amtk::launch_pass2_colsum(s, q, k, lse_buf, colsum, stream);
+    if (e == hipSuccess && (stage == 0 || stage == 3))
+      e = amtk::launch_block_topk(s, sp.query_block, sp.k, colsum, idx, count, mass, stream);
+    return e == hipSuccess ? AMTK_OK : hip_fail(e);
+  }
+  const CandidatePool pool = pool_of(ws, L);
   if (stage == 0 || stage == 1) {
     e = amtk::launch_pass1_lse(s, q, k, lse_buf, pool.ovf_count, stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -264,6 +289,7 @@ int amtk_pool_stats(const amtk_attn_desc* attn, const amtk_support_desc* sup, co
   if (rc) return rc;
   if ((rc = check_support(sup))) return rc;
   if (!ws || !max_candidates || !overflow_rows || !capacity) return AMTK_E_INVALID;
+  if (sup->query_block != 1) return AMTK_E_UNSUPPORTED;   // selection blocks keep no pools
   const Layout L = layout(s, *sup);
   if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -45,6 +45,18 @@ hipError_t launch_pass2_filter(const LayerShape& s, int key_block, int budget, c
                                const void* k, const float* lse, const CandidatePool& pool,
                                hipStream_t stream);
 
+// Selection blocks of consecutive queries: column sums of the head-averaged
+// mass over each 32-row tile, colsum[tile][j] (keys j up to the tile's last
+// row), in place of the per-row filter.
+hipError_t launch_pass2_colsum(const LayerShape& s, const void* q, const void* k, const float* lse,
+                               float* colsum, hipStream_t stream);
+
+// The shared top-k of each selection block of bsel rows (a multiple of 32)
+// from those column sums, written into the index row of every query of the
+// block (ascending ids, -1 padding), with the block scores as masses.
+hipError_t launch_block_topk(const LayerShape& s, int bsel, int budget, const float* colsum,
+                             int32_t* idx, int32_t* count, float* mass, hipStream_t stream);
+
 // Exact top-k from each row's candidates (rows whose pool did not overflow),
 // then the dense recompute + select for rows that did.
 hipError_t launch_select(const LayerShape& s, int key_block, int budget, const void* q,

@@ -363,12 +363,16 @@ __device__ __forceinline__ int part_index(int g, int r, int src_lane) {
   return (g * 16 + r) * 64 + (src_lane ^ (4 * r));
 }
 
-template <typename T, int D, int G, int KB, int HK>   // HK: the KV heads if fixed at 8, else 0
+// HK: the KV heads if fixed at 8, else 0. CS: instead of filtering each
+// row, write the column sums of the mass over the tile's rows (selection
+// blocks of consecutive queries share one support; KB = 1 only).
+template <typename T, int D, int G, int KB, int HK, bool CS>
 __global__ __launch_bounds__(512) void pass2_filter_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ lse, int n,
     int hkv_arg, float c, float inv_hq, int budget, uint2* __restrict__ cand, int cap,
     int* __restrict__ cand_count, int* __restrict__ row_bin, int* __restrict__ ovf_count,
-    int* __restrict__ ovf_list) {
+    int* __restrict__ ovf_list, float* __restrict__ colsum) {
+  static_assert(!CS || KB == 1, "column sums are per token");
   const int hkv = HK ? HK : hkv_arg;
   typedef KTile<T, D> KT;
   constexpr int NC = KT::kChunks;
@@ -502,6 +506,28 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[wb ^ (68 * r)] = pacc[r];
       barrier_lds();   // partial masses visible
+      if constexpr (CS) {
+        // ---- column sums: sum over the tile's rows i < n of P_i(j) for each
+        // of its 32 keys (2*hkv threads per key, 16/hkv rows each; the causal
+        // zeros of the diagonal tile are already in the partials), summed in
+        // a fixed order
+        const float* pb = part + (kt & 1) * part_floats;
+        const int tpk = 2 * hkv, key = (int)threadIdx.x / tpk, j0 = (int)threadIdx.x % tpk;
+        const int r = ((key >> 3) << 2) | (key & 3), h2 = (key >> 2) & 1;
+        float sum = 0.f;
+        for (int e = 0; e < 16 / hkv; ++e) {
+          const int qq = j0 + tpk * e;
+          if (q0 + qq < n) {
+            const float* src = pb + part_index(0, r, qq + 32 * h2);
+            float p = src[0];
+            for (int gg = 1; gg < hkv; ++gg) p += src[gg * 16 * 64];
+            sum += p;
+          }
+        }
+        for (int sh = 1; sh < tpk; sh <<= 1) sum += __shfl_xor(sum, sh, 64);
+        if (j0 == 0 && k0 + key < n) colsum[(size_t)qt * n + k0 + key] = sum * inv_hq;
+        continue;
+      }
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       // A mass passes the bound bin exactly when its bit pattern is at least
       // the bin's floor pattern, so the bin itself is only formed for the
@@ -594,6 +620,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     }
   }
   wait_vmem_all();
+  if constexpr (CS) return;
   __syncthreads();
   if (threadIdx.x < 32) {
     const int qq = q0 + threadIdx.x;
@@ -637,14 +664,32 @@ static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, cons
                             const float* lse, const CandidatePool& pool, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
   const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB);
-  auto kern = s.hkv == 8 ? pass2_filter_kernel<T, D, G, KB, 8> : pass2_filter_kernel<T, D, G, KB, 0>;
+  auto kern = s.hkv == 8 ? pass2_filter_kernel<T, D, G, KB, 8, false>
+                         : pass2_filter_kernel<T, D, G, KB, 0, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
                      s.scale * kLog2e, 1.0f / (float)s.hq, budget, pool.cand, pool.cap, pool.count,
-                     pool.bin, pool.ovf_count, pool.ovf_list);
+                     pool.bin, pool.ovf_count, pool.ovf_list, nullptr);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+static hipError_t run_pass2_colsum(const LayerShape& s, const void* q, const void* k,
+                                   const float* lse, float* colsum, hipStream_t stream) {
+  const int ntiles = (s.n + 31) / 32;
+  const size_t lds = pass2_lds_bytes<T, D>(s.hkv, 1);
+  auto kern = s.hkv == 8 ? pass2_filter_kernel<T, D, G, 1, 8, true>
+                         : pass2_filter_kernel<T, D, G, 1, 0, true>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
+                     s.scale * kLog2e, 1.0f / (float)s.hq, 0, nullptr, 0, nullptr, nullptr, nullptr,
+                     nullptr, colsum);
   return hipGetLastError();
 }
 
@@ -699,6 +744,11 @@ static hipError_t run_pass2_kb(const LayerShape& s, int key_block, int budget, c
   if (key_block == 1) return run_pass2<T, D, G, 1>(s, budget, q, k, lse, pool, stream);
   if (key_block == 64) return run_pass2<T, D, G, 64>(s, budget, q, k, lse, pool, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pass2_colsum(const LayerShape& s, const void* q, const void* k, const float* lse,
+                               float* colsum, hipStream_t stream) {
+  AMTK_PASS_DISPATCH(run_pass2_colsum, s, q, k, lse, colsum, stream);
 }
 
 hipError_t launch_pass2_filter(const LayerShape& s, int key_block, int budget, const void* q,

@@ -70,7 +70,8 @@ def _topk(lib, a, s, ws_bytes=1, q=FAKE, ws=FAKE, idx=FAKE):
 @pytest.mark.parametrize("kw,code", [
     (dict(n=0), -1), (dict(hq=6, hkv=4), -1), (dict(dtype=7), -1), (dict(scale=float("nan")), -1),
     (dict(k=0), -1), (dict(cap=-1), -1),
-    (dict(causal=0), -2), (dict(d=96), -2), (dict(kb=2), -2), (dict(qb=64), -2), (dict(k=9000), -2),
+    (dict(causal=0), -2), (dict(d=96), -2), (dict(kb=2), -2), (dict(qb=32), -2), (dict(qb=64, kb=64), -2),
+    (dict(k=9000), -2),
     (dict(hq=32, hkv=2), -2),          # 16 query heads per KV head
     (dict(hkv=16, hq=16), -2),         # more KV heads than pass waves
     (dict(dtype=1, d=128, hq=8, hkv=2), -2),   # fp32 group tile too large for registers
@@ -110,6 +111,20 @@ def test_workspace_sizes_grow_with_n_and_cap(lib):
     lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s1), ctypes.byref(b1))
     lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s2), ctypes.byref(b2))
     assert b2.value - b1.value >= 4096 * 90 * 8
+
+
+def test_selection_block_workspace_and_pool_stats(lib):
+    """query_block = 64 keeps the LSE and the 32-row tiles' column sums
+    ((n+31)/32 x n floats) instead of candidate pools, and has no pool stats."""
+    n, hq = 4096, 8
+    a, s = _descs(n=n, hq=hq, qb=64)
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s), ctypes.byref(need)) == 0
+    assert need.value >= (n + 31) // 32 * n * 4 + hq * n * 4
+    assert need.value < (n + 31) // 32 * n * 4 + hq * n * 4 + 4096
+    z = ctypes.c_int64(0)
+    assert lib.amtk_pool_stats(ctypes.byref(a), ctypes.byref(s), FAKE, need.value, ctypes.byref(z),
+                               ctypes.byref(z), ctypes.byref(z), None) == -2
 
 
 def test_sparse_attn_validation(lib):

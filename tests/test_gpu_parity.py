@@ -300,6 +300,65 @@ def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block):
         assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
 
 
+# ------------------------------------------------ selection-block-shared support
+def _check_query_blocks(amtk, x, dtype, k, blocks=None, b_sel=64):
+    """oracle_prefill with query_block = b_sel against the oracle's block
+    supports: every row of a block carries the block's support, the support
+    passes the near-tie check against the block scores, the masses are the
+    block scores, and each row's output matches the oracle on the shared
+    keys up to that row."""
+    from tests.support_rules import check_row
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    d_ = upload(x, dtype)
+    out, idx, count, mass, _ = amtk.oracle_prefill(d_["q"], d_["k"], d_["v"], k,
+                                                   query_block=b_sel)
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    count, mass = count.cpu().numpy(), mass.cpu().numpy()
+    n = x["q"].shape[0]
+    nblk = (n + b_sel - 1) // b_sel
+    for t in (range(nblk) if blocks is None else blocks):
+        r = layer.query_block(int(t), k, b_sel)
+        rows = list(r["rows"])
+        i0 = rows[0]
+        for i in rows:
+            assert count[i] == count[i0] and np.array_equal(idx[i], idx[i0]), f"row {i}"
+        ok, msg, _ = check_row(idx[i0], count[i0], r["score"], r["kth"], k)
+        assert ok, f"block {t}: {msg}"
+        sel = idx[i0, : count[i0]]
+        np.testing.assert_allclose(mass[i0, : count[i0]], r["score"][sel], rtol=2e-4, atol=1e-7)
+        for i in rows:
+            sup = sel[sel <= i]
+            if sup.size == 0:
+                assert np.all(out[i] == 0), f"row {i}"
+                continue
+            o_ref, _ = layer.attention_on(i, sup)
+            err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
+            assert err <= TOL_OUT[dtype], f"row {i}: max abs err {err}"
+
+
+@pytest.mark.parametrize("n,hq,hkv,d,dtype,k", [
+    (200, 8, 2, 64, "f32", 12),      # 4 blocks, the last with 8 rows
+    (330, 32, 8, 128, "bf16", 40),   # the MFMA attention path, last block 10 rows
+    (129, 4, 4, 64, "bf16", 70),     # budgets above the first blocks' key counts
+    (64, 2, 1, 128, "f32", 5),       # one block
+])
+def test_query_blocks_small_shapes(gpu_lib, n, hq, hkv, d, dtype, k):
+    x = random_inputs(n, hq, hkv, d, dtype, seed=n + k, sink=True)
+    _check_query_blocks(gpu_lib, x, dtype, k)
+
+
+def test_query_blocks_mid_bf16_4k_sampled(gpu_lib):
+    w = WORKLOADS["mid_bf16_4k"]
+    x = generate(w)
+    _check_query_blocks(gpu_lib, x, "bf16", w.k, blocks=[0, 1, 7, 30, 63])
+
+
+def test_query_blocks_long_bf16_32k_sampled(gpu_lib):
+    w = WORKLOADS["long_bf16_32k"]
+    x = generate(w)
+    _check_query_blocks(gpu_lib, x, "bf16", w.k, blocks=[3, 170, 511])
+
+
 # ------------------------------------------------------------ the workloads
 def _workload_check(amtk, name, rows_cap=None, n=None):
     w = WORKLOADS[name]
