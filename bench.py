@@ -29,6 +29,9 @@ KERNEL_SOURCES = {
     "pass2_filter": "sparse_long_context_causal_amd/csrc/passes.hip",
     "select": "sparse_long_context_causal_amd/csrc/select.hip",
     "sparse_attn": "sparse_long_context_causal_amd/csrc/sparse_attn.hip",
+    "pass2_colsum": "sparse_long_context_causal_amd/csrc/passes.hip",
+    "block_topk": "sparse_long_context_causal_amd/csrc/block_select.hip",
+    "sparse_attn_blocks": "sparse_long_context_causal_amd/csrc/block_attn.hip",
 }
 
 
@@ -60,15 +63,21 @@ def support_tokens(plan, key_block, query_block=1):
     return int(torch.where(valid, toks, torch.zeros_like(toks)).sum().item())
 
 
-def algorithmic_work(w, n, k, sup):
-    """Per-launch algorithmic flops / bytes of each kernel (see the design notes)."""
+def algorithmic_work(w, n, k, sup, gathered=None, units_read=None):
+    """Per-launch algorithmic flops / bytes of each kernel (see the design notes).
+
+    sup: keys attended over all rows; gathered: key rows the sparse kernel
+    must fetch (= sup per row; once per selection block when shared);
+    units_read: index entries it reads."""
     e = 2 if w.dtype == "bf16" else 4
+    gathered = sup if gathered is None else gathered
+    units_read = n * k if units_read is None else units_read
     pairs = n * (n + 1) // 2                    # causal query-key pairs
     qk_flops = 2 * w.d * w.hq * pairs           # one QK^T over the causal triangle
-    attn_bytes = (sup * w.hkv * w.d * 2 * e     # gathered K and V rows
+    attn_bytes = (gathered * w.hkv * w.d * 2 * e   # gathered K and V rows
                   + n * w.hq * w.d * e          # Q
                   + n * w.hq * w.d * 4          # O (fp32)
-                  + n * k * 4 + n * 4)          # idx, count
+                  + units_read * 4 + n * 4)     # idx, count
     return qk_flops, attn_bytes
 
 
@@ -234,7 +243,14 @@ def main():
 
     n = w.n
     sup = support_tokens(plan, w.key_block, qb)
-    qk_flops, attn_bytes = algorithmic_work(w, n, k, sup)
+    gathered = units_read = None
+    attn_name = "sparse_attn"
+    if qb != 1 and plan.shared_tiles:   # one gather per selection block
+        attn_name = "sparse_attn_blocks"
+        first = plan.count[::qb].to(torch.int64)
+        gathered = int(first.sum().item())
+        units_read = gathered
+    qk_flops, attn_bytes = algorithmic_work(w, n, k, sup, gathered, units_read)
     peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kernels = {}
     if w.indexer_d:
@@ -244,7 +260,7 @@ def main():
         kernels["pass1_lse"] = {"bound": "mfma", "work": qk_flops, "ms": per["pass1_lse"]}
         kernels[names[1]] = {"bound": "mfma", "work": qk_flops, "ms": per[names[1]]}
         kernels[names[2]] = {"bound": "alu", "work": None, "ms": per[names[2]]}
-    kernels["sparse_attn"] = {"bound": "hbm", "work": attn_bytes, "ms": per["sparse_attn"]}
+    kernels[attn_name] = {"bound": "hbm", "work": attn_bytes, "ms": per["sparse_attn"]}
     dom = max((kn for kn in kernels if kernels[kn]["work"]), key=lambda kn: kernels[kn]["ms"])
     kd = kernels[dom]
     if kd["bound"] == "hbm":
@@ -293,7 +309,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) Q/K/V, sink key, planted needle keys)",
-        "config": {"workload": w.name, "n": n, "hq": w.hq, "hkv": w.hkv, "d": w.d, "k": k,
+        "config": {"workload": w.name if qb == 1 else f"{w.name}_qb{qb}", "n": n, "hq": w.hq,
+                   "hkv": w.hkv, "d": w.d, "k": k,
                    "key_block": w.key_block, "query_block": qb, "support_tokens": sup,
                    "parallelism": "none"},
         "roofline": roof,

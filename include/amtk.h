@@ -145,10 +145,37 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
                 float* lse_sparse, void* stream);
 
 /*
+ * sparse_attn_blocks - attention of each selection block's queries on the
+ * block's shared support, the keys gathered once per block.
+ * [TB 2.1]: with selection-block-shared granularity one support set serves
+ * a block of query_block consecutive queries; each query i then attends
+ * over the shared keys j <= i, softmax renormalised over them.
+ * Block t holds rows t*query_block .. min((t+1)*query_block, n) - 1; its
+ * support is idx[t*query_block][0..count[t*query_block]) (token ids, any
+ * order, distinct), i.e. the first row of the block in the [n][max_units]
+ * layout topk_support writes with sup->query_block = query_block. The other
+ * rows' entries are not read. Per row, ids < 0, ids >= n and ids > i are
+ * skipped; a row left with no key gets O = 0 and LSE = -inf. The result
+ * equals sparse_attn (key_block = 1) when every row of a block holds the
+ * block's support.
+ * Shapes: bf16, d = 128, hkv = 8, hq = 32, query_block = 64; anything else
+ * returns AMTK_E_UNSUPPORTED (sparse_attn covers it row by row).
+ *
+ * idx       : [n][max_units] int32 (device); count: [n] int32 (device).
+ * o         : OUT [n][hq][d] fp32.
+ * lse_sparse: OUT [hq][n] fp32 log-sum-exp over each row's keys, or NULL.
+ */
+int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t query_block, int32_t max_units,
+                       const void* q, const void* k, const void* v, const int32_t* idx,
+                       const int32_t* count, float* o, float* lse_sparse, void* stream);
+
+/*
  * oracle_prefill - topk_support followed by sparse_attn on the same stream:
  * the oracle's full per-layer step (dense mass -> top-k support -> sparse
  * recompute with the original Q/K/V), [TB 2.1], [Abstract].
  * Arguments as in the two calls above; idx and count are required outputs.
+ * With sup->query_block = 64 the sparse step is sparse_attn_blocks where it
+ * supports the shape, else sparse_attn on the per-row copies.
  */
 int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
                    const void* k, const void* v, float* o, int32_t* idx, int32_t* count,

@@ -10,6 +10,7 @@ raises.
 Functions (names follow the C ABI):
   topk_support(q, k, budget, key_block=1)      -> idx, count, mass, lse
   sparse_attn(q, k, v, idx, count, key_block)  -> out, lse_sparse
+  sparse_attn_blocks(q, k, v, idx, count, query_block=64) -> out, lse_sparse
   oracle_prefill(q, k, v, budget, key_block=1) -> out, idx, count, mass, lse
   indexer_topk(q_idx, k_idx, budget, key_block=64) -> idx, count, mass
 q: [N, Hq, d], k/v: [N, Hkv, d], bf16 or fp32 CUDA (HIP) tensors, contiguous.
@@ -152,6 +153,29 @@ def sparse_attn(q, k, v, idx, count, key_block: int = 1, scale: Optional[float] 
     return out, lse
 
 
+def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64,
+                       scale: Optional[float] = None, want_lse: bool = False, out=None):
+    """Attention of each selection block of query_block rows on the support in
+    the block's first row (rows skip ids after themselves). Returns
+    (out [N,Hq,d] fp32, lse_sparse [Hq,N] or None)."""
+    torch = _torch()
+    _check_dev(q, k, v, idx, count)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    if idx.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("idx and count must be int32")
+    ad = attn_desc(q, k, scale)
+    n, hq, d = q.shape
+    if idx.dim() != 2 or idx.shape[0] != n or count.shape != (n,):
+        raise ValueError("idx must be [N, max_units] and count [N]")
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=q.device) if want_lse else None
+    _call("sparse_attn_blocks", ctypes.byref(ad), int(query_block), int(idx.shape[1]), _ptr(q),
+          _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _stream(q.device))
+    return out, lse
+
+
 def oracle_prefill(q, k, v, budget: int, key_block: int = 1, scale: Optional[float] = None,
                    candidate_cap: int = 0, want_mass: bool = True, want_lse: bool = True,
                    ws=None, query_block: int = 1):
@@ -204,7 +228,8 @@ def pool_stats(ad: AttnDesc, sd: SupportDesc, ws, device=None):
     return mx.value, ov.value, cap.value
 
 
-__all__ = ["load", "topk_support", "sparse_attn", "oracle_prefill", "indexer_topk",
+__all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_blocks", "oracle_prefill",
+           "indexer_topk",
            "topk_workspace_bytes", "indexer_workspace_bytes", "workspace", "pool_stats",
            "attn_desc", "support_desc", "AmtkError", "AttnDesc", "SupportDesc"]
 
@@ -241,6 +266,10 @@ class PrefillPlan:
         self.mass = torch.empty((self.n, budget), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.hq, self.n), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.n, self.hq, self.d), dtype=torch.float32, device=dev)
+        # the block tile kernel's shapes (sparse_attn_blocks); elsewhere the
+        # per-row kernel reads the rows' copies of their block's support
+        self.shared_tiles = (q.dtype == torch.bfloat16 and self.d == 128 and self.hq == 32
+                             and k.shape[1] == 8 and query_block == 64)
 
     def stage(self, s):
         if self.indexer:
@@ -256,6 +285,12 @@ class PrefillPlan:
               _stream(self.q.device))
 
     def attn(self):
+        qb = self.sd.query_block
+        if qb != 1 and self.shared_tiles:
+            _call("sparse_attn_blocks", ctypes.byref(self.ad), qb, self.budget, _ptr(self.q),
+                  _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count), _ptr(self.out),
+                  None, _stream(self.q.device))
+            return
         _call("sparse_attn", ctypes.byref(self.ad), self.key_block, self.budget, _ptr(self.q),
               _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count), _ptr(self.out), None,
               _stream(self.q.device))

@@ -226,6 +226,24 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
   return AMTK_OK;
 }
 
+int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t query_block, int32_t max_units,
+                       const void* q, const void* k, const void* v, const int32_t* idx,
+                       const int32_t* count, float* o, float* lse_sparse, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if (max_units < 1) return AMTK_E_INVALID;
+  if (!amtk::shared_attn_shape_supported(s, query_block)) return AMTK_E_UNSUPPORTED;
+  if (!q || !k || !v || !idx || !count || !o) return AMTK_E_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
+      !aligned(count, 4) || !aligned(o, 16) || (lse_sparse && !aligned(lse_sparse, 4)))
+    return AMTK_E_INVALID;
+  hipError_t e = amtk::launch_shared_attn(s, query_block, max_units, q, k, v, idx, count, o,
+                                          lse_sparse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
 int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
                    const void* k, const void* v, float* o, int32_t* idx, int32_t* count,
                    float* mass, float* lse, void* ws, size_t ws_bytes, void* stream) {
@@ -239,8 +257,13 @@ int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = run_topk(s, *sup, 0, q, k, idx, count, mass, lse, ws, ws_bytes, st);
   if (rc) return rc;
+  // selection blocks: one gather per block where the tile kernel covers the
+  // shape; every row also holds its block's support, so the per-row kernel
+  // gives the same result elsewhere
   hipError_t e =
-      amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o, nullptr, st);
+      sup->query_block != 1 && amtk::shared_attn_shape_supported(s, sup->query_block)
+          ? amtk::launch_shared_attn(s, sup->query_block, sup->k, q, k, v, idx, count, o, nullptr, st)
+          : amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o, nullptr, st);
   if (e != hipSuccess) return hip_fail(e);
   return AMTK_OK;
 }

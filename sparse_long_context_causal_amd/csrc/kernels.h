@@ -69,6 +69,16 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream);
 
+// Attention of each selection block's queries on the block's shared
+// support: the ids and count of the block's first row serve all of its rows,
+// each row skipping the ids after it. bf16, d = 128, 8 KV heads x 4 query
+// heads, blocks of 64 queries (shared_attn_shape_supported).
+hipError_t launch_shared_attn(const LayerShape& s, int query_block, int max_units, const void* q,
+                              const void* k, const void* v, const int32_t* idx,
+                              const int32_t* count, float* o, float* lse_sparse,
+                              hipStream_t stream);
+bool shared_attn_shape_supported(const LayerShape& s, int query_block);
+
 bool pass_shape_supported(const LayerShape& s);
 bool sparse_shape_supported(const LayerShape& s);
 

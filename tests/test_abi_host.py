@@ -135,6 +135,20 @@ def test_sparse_attn_validation(lib):
     assert f(ctypes.byref(a), 1, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
 
 
+def test_sparse_attn_blocks_validation(lib):
+    f = lib.sparse_attn_blocks
+    a, _ = _descs()
+    assert f(ctypes.byref(a), 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    # the tile kernel's shape only: bf16, d = 128, 8 KV x 4 query heads, blocks of 64
+    assert f(ctypes.byref(a), 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    from sparse_long_context_causal_amd import _abi
+    b = _abi.AttnDesc(1000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    assert f(ctypes.byref(b), 32, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert f(ctypes.byref(b), 64, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
+    odd = ctypes.c_void_p(0x100004)   # o must be 16-byte aligned
+    assert f(ctypes.byref(b), 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, odd, None, None) == -1
+
+
 def test_indexer_validation(lib):
     _, s = _descs(kb=64, k=16)
     f = lib.indexer_topk

@@ -359,6 +359,86 @@ def test_query_blocks_long_bf16_32k_sampled(gpu_lib):
     _check_query_blocks(gpu_lib, x, "bf16", w.k, blocks=[3, 170, 511])
 
 
+def test_sparse_attn_blocks_oracle_supports(gpu_lib):
+    """The block tile kernel alone, on the oracle's own block supports: every
+    row against the oracle's output and support LSE. Only the first row of a
+    block carries the support (the others hold junk the kernel must not read)."""
+    import torch
+    amtk = gpu_lib
+    n, k = 330, 40                      # 6 blocks, the last with 10 rows; 2 chunks of keys
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=44, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    idx = np.full((n, k), -5, dtype=np.int32)
+    cnt = np.full(n, 7, dtype=np.int32)
+    res = {}
+    for t in range((n + 63) // 64):
+        r = layer.query_block(t, k, 64)
+        res[t] = r
+        u = r["units"]
+        idx[64 * t, :] = -1
+        idx[64 * t, : u.size] = u
+        cnt[64 * t] = u.size
+    d = upload(x, "bf16")
+    out, lse = amtk.sparse_attn_blocks(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
+                                       torch.from_numpy(cnt).cuda(), 64, want_lse=True)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in range(n):
+        r = res[i // 64]
+        err = float(np.max(np.abs(out[i].astype(np.float64) - r["out"][i])))
+        assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
+        if np.all(np.isneginf(r["lse_s"][i])):
+            assert np.all(np.isneginf(lse[:, i])), f"row {i} lse"
+        else:
+            assert np.max(np.abs(lse[:, i] - r["lse_s"][i])) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
+
+
+def test_sparse_attn_blocks_unsorted_invalid_and_clamped(gpu_lib):
+    """The block tile kernel on hand-made block supports: ids in random order,
+    negative ids, ids past n and past the rows mixed in, a count above
+    max_units (clamped), an empty block, a block whose keys all lie after
+    its first 40 rows (those rows get zeros), a single-chunk block. Every row
+    against the oracle on the ids the contract keeps."""
+    import torch
+    amtk = gpu_lib
+    n, max_units = 300, 100             # 5 blocks, the last with 44 rows; up to 4 chunks
+    rng = np.random.default_rng(91)
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=45, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    idx = np.full((n, max_units), -1, dtype=np.int32)
+    cnt = np.zeros(n, dtype=np.int32)
+    blocks = {}
+    for t in range(5):
+        i0, i1 = 64 * t, min(64 * t + 63, n - 1)
+        if t == 0:
+            ids = rng.permutation(i1 + 1)[:20].tolist()                     # one chunk
+        elif t == 2:
+            ids = (i0 + 40 + rng.permutation(i1 - i0 - 39)).tolist()        # after row i0+39
+        else:
+            ids = rng.permutation(i1 + 1)[:90].tolist() + [-1, n + 3, -7, i1 + 1, 2 ** 30]
+            ids = rng.permutation(np.asarray(ids, dtype=np.int64)).tolist()
+        c = len(ids)
+        if t == 3:
+            c = max_units + 9                                               # clamped
+        if t == 4:
+            ids, c = [], 0
+        idx[i0, : min(len(ids), max_units)] = ids[:max_units]
+        cnt[i0] = c
+        blocks[t] = [int(u) for u in idx[i0, : min(c, max_units)] if 0 <= u < n]
+    d = upload(x, "bf16")
+    out, lse = amtk.sparse_attn_blocks(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
+                                       torch.from_numpy(cnt).cuda(), 64, want_lse=True)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in range(n):
+        toks = [j for j in blocks[i // 64] if j <= i]
+        if not toks:
+            assert np.all(out[i] == 0) and np.all(np.isneginf(lse[:, i])), f"row {i}"
+            continue
+        o_ref, l_ref = layer.attention_on(i, toks)
+        err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
+        assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
+        assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
+
+
 # ------------------------------------------------------------ the workloads
 def _workload_check(amtk, name, rows_cap=None, n=None):
     w = WORKLOADS[name]
