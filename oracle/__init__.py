@@ -8,8 +8,10 @@ raises when the HIP extension is missing instead of falling back to this.
 from .attention_mass import (OracleLayer, IndexerOracle, row_logits, log_sum_exp, head_mass,
                              top_units, kth_score, block_masses, tokens_of_blocks,
                              support_attention, dense_attention, causal_sparsity,
-                             default_scale, kv_head, query_block_rows)
+                             default_scale, kv_head, query_block_rows, captured_mass,
+                             support_overlap)
 
 __all__ = ["OracleLayer", "IndexerOracle", "row_logits", "log_sum_exp", "head_mass",
            "top_units", "kth_score", "block_masses", "tokens_of_blocks", "support_attention",
-           "dense_attention", "causal_sparsity", "default_scale", "kv_head", "query_block_rows"]
+           "dense_attention", "causal_sparsity", "default_scale", "kv_head", "query_block_rows",
+           "captured_mass", "support_overlap"]

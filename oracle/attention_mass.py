@@ -11,8 +11,10 @@ Long-Context Models" (arXiv 2606.07703). It is cited in two places:
   [Abstract]  the authors' abstract (searcharxiv.org page, "Abstract");
   [TB 2.1]    the gist.science page, "Technischer Bericht", section 2.1 (the
               attention-mass top-k oracle); [TB 2.2] is its section 2.2 (the
-              head-collapsed indexer) and [TB 3.1] its section 3.1 (oracle
-              feasibility, with the sparsity range of the 4K-100K sweep).
+              head-collapsed indexer), [TB 2.3] its section 2.3 (the oracle,
+              indexer and realization gaps) and [TB 3.1] its section 3.1
+              (oracle feasibility, with the sparsity range of the 4K-100K
+              sweep).
 Readings of points those pages leave open are marked READING; each one is
 listed in the design notes of the repository.
 
@@ -174,6 +176,32 @@ def causal_sparsity(n: int, k: int) -> float:
     return float(1.0 - kept / ((n * (n + 1)) / 2.0))
 
 
+def captured_mass(p: np.ndarray, support: np.ndarray) -> float:
+    """Head-averaged dense mass a support keeps: sum over j in S of P_i(j).
+
+    [TB 2.3] splits a sparse layer's loss into the oracle gap (oracle support
+    against dense attention), the indexer gap (an indexer's support in place
+    of the oracle's) and the realization gap (runtime constraints such as
+    selection-block sharing). READING: at the level of one layer their
+    synthetic analogue is the share of the dense head-averaged mass P_i
+    (which sums to 1) that a support keeps. p is row i's mass [i+1]; support
+    holds token ids <= i.
+    """
+    sup = np.asarray(support, dtype=np.int64)
+    return float(p[sup].sum()) if sup.size else 0.0
+
+
+def support_overlap(a: Sequence[int], b: Sequence[int]) -> int:
+    """Number of ids two supports share (negative ids never count).
+
+    [TB 2.3]: the indexer gap compares an indexer's support with the
+    oracle's; overlap / |a| is the recall of support a by support b.
+    """
+    a = np.asarray(a, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    return int(np.intersect1d(a[a >= 0], b[b >= 0]).size)
+
+
 def query_block_rows(t: int, b_sel: int, n: int) -> range:
     """Query rows of selection block t: b_sel consecutive rows, the last block
     holding what is left of [0, N)."""
@@ -264,6 +292,11 @@ class OracleLayer:
         """Sparse output of row i on a given support (used with the GPU's support)."""
         sup = np.asarray(sorted(int(j) for j in support), dtype=np.int64)
         return support_attention(self.logits(i), self.v_t, sup)
+
+    def captured(self, i: int, support: Sequence[int]) -> float:
+        """Head-averaged dense mass of row i on a given token support ([TB 2.3])."""
+        s = self.logits(i)
+        return captured_mass(head_mass(s, log_sum_exp(s)), np.asarray(support, dtype=np.int64))
 
     def dense(self, i: int) -> np.ndarray:
         s = self.logits(i)

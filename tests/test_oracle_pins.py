@@ -282,6 +282,62 @@ def test_nesting_causality_and_capture_bound():
             prev = s
 
 
+# ------------------------------------------------------------ diagnostics
+def test_captured_mass_of_full_support_is_one_and_of_top_k_is_brute_force_top_sum():
+    """Captured mass pins: the whole causal prefix keeps all of the mass (P
+    sums to 1); the oracle's top-k keeps the sum of the k largest entries of
+    the brute-force mass row; it never decreases with k."""
+    for (n, hq, hkv, d), seed in (((40, 4, 2, 8), 1), ((64, 6, 3, 16), 2)):
+        x = random_inputs(n, hq, hkv, d, "f32", seed=seed + 50, sink=True)
+        layer = OracleLayer(x["q"], x["k"], x["v"])
+        P, _, _ = bf.full_mass(x["q"], x["k"], oracle.default_scale(d))
+        for i in range(0, n, 3):
+            assert abs(layer.captured(i, np.arange(i + 1)) - 1.0) <= 1e-12
+            prev = 0.0
+            for kk in (1, 3, 8, 20, n):
+                r = layer.row(i, kk)
+                top = np.sort(P[i, : i + 1])[::-1][: min(kk, i + 1)].sum()
+                assert abs(layer.captured(i, r["units"]) - top) <= 1e-12
+                assert abs(r["captured"] - top) <= 1e-12
+                assert r["captured"] >= prev - 1e-15
+                prev = r["captured"]
+
+
+def test_captured_mass_from_support_lse_identity():
+    """The identity the GPU's captured mass rests on:
+    sum_{j in S} P(j) = (1/Hq) sum_h exp(LSE^S_h - LSE_h), checked between the
+    oracle's support attention (LSE over S) and its mass row, on random
+    supports, including an empty one (LSE^S = -inf contributes 0)."""
+    x = random_inputs(90, 8, 2, 32, "f32", seed=57, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    rng = np.random.default_rng(5)
+    for i in (0, 1, 17, 60, 89):
+        s = layer.logits(i)
+        lse = oracle.log_sum_exp(s)
+        for m in (0, 1, 5, i + 1):
+            sup = np.sort(rng.permutation(i + 1)[:m])
+            want = layer.captured(i, sup)
+            if sup.size == 0:
+                assert want == 0.0
+                continue
+            _, lse_s = oracle.support_attention(s, layer.v_t, sup)
+            got = float(np.mean(np.exp(lse_s - lse)))
+            assert abs(got - want) <= 1e-12 * max(1.0, want)
+
+
+def test_support_overlap_against_sets():
+    rng = np.random.default_rng(8)
+    assert oracle.support_overlap([1, 4, 9], [1, 4, 9]) == 3
+    assert oracle.support_overlap([1, 4, 9], [0, 2, 10]) == 0
+    assert oracle.support_overlap([-1, 3, -1], [-1, 3]) == 1
+    assert oracle.support_overlap([], [1]) == 0
+    for _ in range(50):
+        a = rng.choice(100, size=int(rng.integers(0, 40)), replace=False)
+        b = rng.choice(100, size=int(rng.integers(0, 40)), replace=False)
+        want = len(set(a.tolist()) & set(b.tolist()))
+        assert oracle.support_overlap(a, b) == want
+
+
 def test_needles_are_selected_on_tiny_workload():
     w = WORKLOADS["tiny_fp32_512"]
     x = generate(w)
