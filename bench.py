@@ -158,6 +158,72 @@ def _cpu_baseline_blocks(w, x, k, b_sel, budget_s, threads):
                        f"row length (cost ~ i+1): {full_s:.1f} s")}
 
 
+def diagnostics(amtk, w, x, k):
+    """Support diagnostics of one layer (the layer-level analogues of the
+    oracle, realization and indexer gaps): the mean head-averaged dense mass
+    the oracle's support keeps across budgets, with per-query and with shared
+    selection-block supports, and, on the indexer workload, the indexer's
+    recall of the oracle's blocks and the oracle mass its support keeps.
+    Every per-row figure comes from the library's kernels; the means are
+    taken here."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {key: torch.from_numpy(x[key]).to(tdt).to(dev) for key in ("q", "k", "v")}
+    rep = {"diagnostics": w.name, "n": w.n, "k": k}
+
+    def mean(a):
+        return float(a.to(torch.float64).mean().item())
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if w.indexer_d:
+        kb = w.key_block
+        qi = torch.from_numpy(x["q_idx"]).to(torch.bfloat16).to(dev)
+        ki = torch.from_numpy(x["k_idx"]).to(torch.bfloat16).to(dev)
+        ind, cind, _ = amtk.indexer_topk(qi, ki, k, kb)
+        orc, corc, _, lse = amtk.topk_support(t["q"], t["k"], k, kb)
+        _, lse_i = amtk.sparse_attn(t["q"], t["k"], t["v"], ind, cind, kb, want_lse=True)
+        _, lse_o = amtk.sparse_attn(t["q"], t["k"], t["v"], orc, corc, kb, want_lse=True)
+        ev0.record()
+        cap_i = amtk.captured_mass(lse, lse_i)
+        ov = amtk.support_overlap(orc, corc, ind, cind)
+        ev1.record()
+        cap_o = amtk.captured_mass(lse, lse_o)
+        torch.cuda.synchronize(dev)
+        rep["indexer_block_recall"] = mean(ov.to(torch.float64) / corc.clamp(min=1))
+        rep["indexer_captured_mass"] = mean(cap_i)
+        rep["oracle_block_captured_mass"] = mean(cap_o)
+        rep["ms_captured_and_overlap"] = ev0.elapsed_time(ev1)
+        return rep
+    sweep = {}
+    for kk in sorted({max(1, k // 4), max(1, k // 2), k, 2 * k, 4 * k}):
+        idx, cnt, _, lse = amtk.topk_support(t["q"], t["k"], kk)
+        _, lse_s = amtk.sparse_attn(t["q"], t["k"], t["v"], idx, cnt, 1, want_lse=True)
+        ev0.record()
+        cap = amtk.captured_mass(lse, lse_s)
+        ev1.record()
+        torch.cuda.synchronize(dev)
+        sweep[str(kk)] = {"captured_mass": mean(cap), "min": float(cap.min().item()),
+                          "sparsity": 1.0 - float(cnt.to(torch.float64).sum().item())
+                          / (w.n * (w.n + 1) / 2.0)}
+        if kk == k:
+            rep["ms_captured_mass"] = ev0.elapsed_time(ev1)
+            per_query = cap
+    rep["captured_mass_vs_k"] = sweep
+    if w.dtype == "bf16" and w.hq == 32 and w.hkv == 8 and w.d == 128:
+        idx, cnt, _, lse = amtk.topk_support(t["q"], t["k"], k, query_block=64)
+        _, lse_s = amtk.sparse_attn_blocks(t["q"], t["k"], t["v"], idx, cnt, 64, want_lse=True)
+        cap = amtk.captured_mass(lse, lse_s)
+        rep["captured_mass_blocks_of_64"] = mean(cap)
+        ov = amtk.support_overlap(*amtk.topk_support(t["q"], t["k"], k)[:2], idx, cnt)
+        torch.cuda.synchronize(dev)
+        rep["per_query_ids_kept_by_block_support"] = mean(
+            ov.to(torch.float64) / torch.clamp(torch.arange(1, w.n + 1, device=dev), max=k))
+        rep["captured_mass_per_query"] = mean(per_query)
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +233,8 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="budget (default: the workload's)")
     ap.add_argument("--query-block", type=int, default=1, choices=(1, 64),
                     help="1: a support per query; 64: one support per block of 64 queries")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="only print the support diagnostics of the workload and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -199,6 +267,9 @@ def main():
     k = args.k or w.k
     log(f"[bench] generating {w.name} (n={w.n}, hq={w.hq}, hkv={w.hkv}, d={w.d}, k={k})")
     x = generate(w)
+    if args.diagnostics:
+        print(json.dumps(diagnostics(amtk, w, x, k)), flush=True)
+        return
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     t = {key: torch.from_numpy(x[key]).to(tdt).to(dev) for key in ("q", "k", "v")}

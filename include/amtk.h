@@ -201,6 +201,36 @@ int indexer_topk(int64_t n, int32_t d_idx, int32_t dtype, float scale,
                  int32_t* idx, int32_t* count, float* mass, void* ws, size_t ws_bytes,
                  void* stream);
 
+/*
+ * captured_mass - per row, the head-averaged dense attention mass that a
+ * support keeps: captured[i] = sum_{j in S_i} P_i(j)
+ *                            = (1/hq) sum_h exp(lse_support[h][i] - lse_dense[h][i]).
+ * [TB 2.3]: the layer-level analogue of the oracle, indexer and realization
+ * gaps (how much of the dense mass the oracle's, an indexer's or a shared
+ * block support keeps).
+ * lse_dense  : [hq][n] fp32 dense per-head LSE (topk_support's lse output).
+ * lse_support: [hq][n] fp32 LSE over the support (lse_sparse of sparse_attn
+ *              or sparse_attn_blocks on that support); -inf (an empty
+ *              support) counts 0.
+ * captured   : OUT [n] fp32.
+ */
+int captured_mass(int64_t n, int32_t hq, const float* lse_dense, const float* lse_support,
+                  float* captured, void* stream);
+
+/*
+ * support_overlap - per row, the number of ids two supports share
+ * (overlap / count_a is the recall of support a by support b).
+ * [TB 2.3]: the indexer gap compares an indexer's support with the oracle's.
+ * idx_a [n][max_a], count_a [n]; idx_b [n][max_b], count_b [n]: the ids of
+ * each row ascend within its count (as topk_support and indexer_topk write
+ * them); counts are clamped to [0, max]; both supports use the same units
+ * (tokens, or key blocks). Negative ids never match.
+ * overlap: OUT [n] int32.
+ */
+int support_overlap(int64_t n, int32_t max_a, const int32_t* idx_a, const int32_t* count_a,
+                    int32_t max_b, const int32_t* idx_b, const int32_t* count_b,
+                    int32_t* overlap, void* stream);
+
 /* Message for an AMTK_* code. Never NULL. */
 const char* amtk_strerror(int code);
 

@@ -11,6 +11,8 @@ Functions (names follow the C ABI):
   topk_support(q, k, budget, key_block=1)      -> idx, count, mass, lse
   sparse_attn(q, k, v, idx, count, key_block)  -> out, lse_sparse
   sparse_attn_blocks(q, k, v, idx, count, query_block=64) -> out, lse_sparse
+  captured_mass(lse_dense, lse_support)        -> captured [N]
+  support_overlap(idx_a, count_a, idx_b, count_b) -> overlap [N]
   oracle_prefill(q, k, v, budget, key_block=1) -> out, idx, count, mass, lse
   indexer_topk(q_idx, k_idx, budget, key_block=64) -> idx, count, mass
 q: [N, Hq, d], k/v: [N, Hkv, d], bf16 or fp32 CUDA (HIP) tensors, contiguous.
@@ -176,6 +178,42 @@ def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64,
     return out, lse
 
 
+def captured_mass(lse_dense, lse_support, out=None):
+    """Per row, the head-averaged dense mass a support keeps, from the dense
+    per-head LSE [Hq,N] and the LSE over the support [Hq,N]. Returns [N] fp32."""
+    torch = _torch()
+    _check_dev(lse_dense, lse_support)
+    if lse_dense.dtype != torch.float32 or lse_support.dtype != torch.float32:
+        raise TypeError("LSE arrays must be float32")
+    if lse_dense.dim() != 2 or lse_support.shape != lse_dense.shape:
+        raise ValueError("lse_dense and lse_support must both be [Hq, N]")
+    hq, n = lse_dense.shape
+    if out is None:
+        out = torch.empty((n,), dtype=torch.float32, device=lse_dense.device)
+    _call("captured_mass", n, hq, _ptr(lse_dense), _ptr(lse_support), _ptr(out),
+          _stream(lse_dense.device))
+    return out
+
+
+def support_overlap(idx_a, count_a, idx_b, count_b, out=None):
+    """Per row, the number of ids two supports share (ids ascending within
+    each row's count). Returns [N] int32."""
+    torch = _torch()
+    _check_dev(idx_a, count_a, idx_b, count_b)
+    for t in (idx_a, count_a, idx_b, count_b):
+        if t.dtype != torch.int32:
+            raise TypeError("ids and counts must be int32")
+    n = idx_a.shape[0]
+    if idx_a.dim() != 2 or idx_b.dim() != 2 or idx_b.shape[0] != n or count_a.shape != (n,) \
+            or count_b.shape != (n,):
+        raise ValueError("idx_a/idx_b must be [N, max] and counts [N]")
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int32, device=idx_a.device)
+    _call("support_overlap", n, int(idx_a.shape[1]), _ptr(idx_a), _ptr(count_a),
+          int(idx_b.shape[1]), _ptr(idx_b), _ptr(count_b), _ptr(out), _stream(idx_a.device))
+    return out
+
+
 def oracle_prefill(q, k, v, budget: int, key_block: int = 1, scale: Optional[float] = None,
                    candidate_cap: int = 0, want_mass: bool = True, want_lse: bool = True,
                    ws=None, query_block: int = 1):
@@ -229,7 +267,7 @@ def pool_stats(ad: AttnDesc, sd: SupportDesc, ws, device=None):
 
 
 __all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_blocks", "oracle_prefill",
-           "indexer_topk",
+           "indexer_topk", "captured_mass", "support_overlap",
            "topk_workspace_bytes", "indexer_workspace_bytes", "workspace", "pool_stats",
            "attn_desc", "support_desc", "AmtkError", "AttnDesc", "SupportDesc"]
 

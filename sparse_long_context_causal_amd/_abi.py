@@ -40,6 +40,8 @@ SIGNATURES = {
     "topk_support_stage": (ctypes.c_int, [_A, _S, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparse_attn": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_attn_blocks": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "captured_mass": (ctypes.c_int, [_I64, _I32, _P, _P, _P, _P]),
+    "support_overlap": (ctypes.c_int, [_I64, _I32, _P, _P, _I32, _P, _P, _P, _P]),
     "oracle_prefill": (ctypes.c_int, [_A, _S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "amtk_indexer_workspace": (ctypes.c_int, [_I64, _I32, _I32, _S, ctypes.POINTER(_SZ)]),
     "indexer_topk": (ctypes.c_int, [_I64, _I32, _I32, ctypes.c_float, _S, _P, _P, _P, _P, _P,

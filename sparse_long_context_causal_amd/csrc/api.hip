@@ -291,6 +291,32 @@ int indexer_topk(int64_t n, int32_t d_idx, int32_t dtype, float scale,
                   static_cast<hipStream_t>(stream));
 }
 
+int captured_mass(int64_t n, int32_t hq, const float* lse_dense, const float* lse_support,
+                  float* captured, void* stream) {
+  if (n < 1 || n > INT32_MAX || hq < 1) return AMTK_E_INVALID;
+  if (!lse_dense || !lse_support || !captured) return AMTK_E_INVALID;
+  if (!aligned(lse_dense, 4) || !aligned(lse_support, 4) || !aligned(captured, 4))
+    return AMTK_E_INVALID;
+  hipError_t e = amtk::launch_captured_mass((int)n, hq, lse_dense, lse_support, captured,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
+int support_overlap(int64_t n, int32_t max_a, const int32_t* idx_a, const int32_t* count_a,
+                    int32_t max_b, const int32_t* idx_b, const int32_t* count_b,
+                    int32_t* overlap, void* stream) {
+  if (n < 1 || n > INT32_MAX || max_a < 1 || max_b < 1) return AMTK_E_INVALID;
+  if (!idx_a || !count_a || !idx_b || !count_b || !overlap) return AMTK_E_INVALID;
+  if (!aligned(idx_a, 4) || !aligned(count_a, 4) || !aligned(idx_b, 4) || !aligned(count_b, 4) ||
+      !aligned(overlap, 4))
+    return AMTK_E_INVALID;
+  hipError_t e = amtk::launch_support_overlap((int)n, max_a, idx_a, count_a, max_b, idx_b,
+                                              count_b, overlap, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
 const char* amtk_strerror(int code) {
   switch (code) {
     case AMTK_OK: return "success";

@@ -79,6 +79,15 @@ hipError_t launch_shared_attn(const LayerShape& s, int query_block, int max_unit
                               hipStream_t stream);
 bool shared_attn_shape_supported(const LayerShape& s, int query_block);
 
+// Diagnostics: captured[i] = (1/hq) sum_h exp(lse_support[h][i] - lse_dense[h][i])
+// (-inf support LSE counts 0); overlap[i] = ids shared by two supports whose
+// ids ascend within their counts.
+hipError_t launch_captured_mass(int n, int hq, const float* lse_dense, const float* lse_support,
+                                float* captured, hipStream_t stream);
+hipError_t launch_support_overlap(int n, int max_a, const int32_t* idx_a, const int32_t* count_a,
+                                  int max_b, const int32_t* idx_b, const int32_t* count_b,
+                                  int32_t* overlap, hipStream_t stream);
+
 bool pass_shape_supported(const LayerShape& s);
 bool sparse_shape_supported(const LayerShape& s);
 

@@ -149,6 +149,18 @@ def test_sparse_attn_blocks_validation(lib):
     assert f(ctypes.byref(b), 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, odd, None, None) == -1
 
 
+def test_diagnostics_validation(lib):
+    odd = ctypes.c_void_p(0x100002)
+    assert lib.captured_mass(0, 8, FAKE, FAKE, FAKE, None) == -1
+    assert lib.captured_mass(10, 0, FAKE, FAKE, FAKE, None) == -1
+    assert lib.captured_mass(10, 8, None, FAKE, FAKE, None) == -1
+    assert lib.captured_mass(10, 8, FAKE, FAKE, odd, None) == -1
+    assert lib.support_overlap(0, 4, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == -1
+    assert lib.support_overlap(10, 0, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == -1
+    assert lib.support_overlap(10, 4, FAKE, FAKE, 4, FAKE, None, FAKE, None) == -1
+    assert lib.support_overlap(10, 4, FAKE, FAKE, 4, FAKE, FAKE, odd, None) == -1
+
+
 def test_indexer_validation(lib):
     _, s = _descs(kb=64, k=16)
     f = lib.indexer_topk
