@@ -11,7 +11,8 @@ Long-Context Models" (arXiv 2606.07703). It is cited in two places:
   [Abstract]  the authors' abstract (searcharxiv.org page, "Abstract");
   [TB 2.1]    the gist.science page, "Technischer Bericht", section 2.1 (the
               attention-mass top-k oracle); [TB 2.2] is its section 2.2 (the
-              head-collapsed indexer), [TB 2.3] its section 2.3 (the oracle,
+              head-collapsed indexer and its KL distillation), [TB 2.3] its
+              section 2.3 (the oracle,
               indexer and realization gaps) and [TB 3.1] its section 3.1
               (oracle feasibility, with the sparsity range of the 4K-100K
               sweep).
@@ -330,3 +331,67 @@ class IndexerOracle:
         return {"lse": lse, "p": p, "score": score, "units": units,
                 "unit_mass": score[units], "kth": kth_score(score, k),
                 "support": support}
+
+
+class KLDistillOracle:
+    """KL-distillation loss of the indexer against the oracle's mass ([TB 2.2]).
+
+    The indexer is trained by KL divergence from the dense head-averaged
+    attention-mass distribution, the backbone frozen. READING: teacher P_i =
+    the oracle's head-averaged mass over keys j <= i (token level); student
+    Q_i = causal softmax over j <= i of t_ij = tau_idx * <q_idx[i], k_idx[j]>
+    (tau_idx = 1/sqrt(d_idx), as in the indexer's scoring); per-row loss
+    KL_i = sum_j P_ij (log P_ij - log Q_ij) (terms with P_ij = 0 count 0);
+    training loss L = (1/N) sum_i KL_i; gradients of L with respect to q_idx
+    and k_idx only (the teacher is a constant):
+      dL/dt_ij = (Q_ij - P_ij) / N,
+      dL/dq_idx[i] = tau_idx sum_j dL/dt_ij k_idx[j],
+      dL/dk_idx[j] = tau_idx sum_{i >= j} dL/dt_ij q_idx[i].
+    """
+
+    def __init__(self, layer: "OracleLayer", q_idx: np.ndarray, k_idx: np.ndarray,
+                 scale: Optional[float] = None):
+        self.layer = layer
+        self.q = np.asarray(q_idx, dtype=np.float64)
+        self.k = np.asarray(k_idx, dtype=np.float64)
+        self.scale = default_scale(self.q.shape[1]) if scale is None else float(scale)
+        self.n = self.q.shape[0]
+
+    def row(self, i: int) -> dict:
+        """Teacher P, student log Q, KL_i and dL/dt (length i+1) of row i."""
+        s = self.layer.logits(i)
+        p = head_mass(s, log_sum_exp(s))
+        t = self.scale * (self.k[: i + 1] @ self.q[i])
+        m = np.max(t)
+        log_q = t - (m + math.log(np.sum(np.exp(t - m))))
+        pos = p > 0
+        kl = float(np.sum(p[pos] * (np.log(p[pos]) - log_q[pos])))
+        dt = (np.exp(log_q) - p) / self.n
+        return {"p": p, "log_q": log_q, "kl": kl, "dt": dt}
+
+    def dq(self, i: int) -> np.ndarray:
+        """dL/dq_idx[i] (needs row i only)."""
+        return self.scale * (self.row(i)["dt"] @ self.k[: i + 1])
+
+    def dk(self, keys: Sequence[int]) -> np.ndarray:
+        """dL/dk_idx[j] for the given keys (needs every row i >= min(keys))."""
+        keys = np.asarray(keys, dtype=np.int64)
+        out = np.zeros((keys.size, self.q.shape[1]))
+        for i in range(int(keys.min()), self.n):
+            dt = self.row(i)["dt"]
+            sel = keys <= i
+            out[sel] += self.scale * np.outer(dt[keys[sel]], self.q[i])
+        return out
+
+    def full(self) -> dict:
+        """Per-row KL, the loss and both gradients over all rows (small N)."""
+        d = self.q.shape[1]
+        kl = np.zeros(self.n)
+        dq = np.zeros((self.n, d))
+        dk = np.zeros((self.n, d))
+        for i in range(self.n):
+            r = self.row(i)
+            kl[i] = r["kl"]
+            dq[i] = self.scale * (r["dt"] @ self.k[: i + 1])
+            dk[: i + 1] += self.scale * np.outer(r["dt"], self.q[i])
+        return {"kl": kl, "loss": float(kl.mean()), "dq": dq, "dk": dk}

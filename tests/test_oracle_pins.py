@@ -338,6 +338,84 @@ def test_support_overlap_against_sets():
         assert oracle.support_overlap(a, b) == want
 
 
+# ------------------------------------------------------- KL distillation
+def _kl_inputs(n, hq, hkv, d, d_idx, seed):
+    x = random_inputs(n, hq, hkv, d, "f32", seed=seed, sink=True)
+    rng = np.random.default_rng(seed + 1)
+    qi = rng.standard_normal((n, d_idx)).astype(np.float32)
+    ki = rng.standard_normal((n, d_idx)).astype(np.float32)
+    return x, qi, ki
+
+
+@pytest.mark.parametrize("shape", [(30, 4, 2, 8, 6), (45, 6, 3, 16, 8)])
+def test_kl_distill_against_autograd_brute_force(shape):
+    """Per-row KL, loss and both gradients against a second formulation: the
+    brute-force teacher mass tensor, the student's masked log_softmax over a
+    full [N, N] score matrix and torch fp64 autograd for the gradients."""
+    n, hq, hkv, d, d_idx = shape
+    x, qi, ki = _kl_inputs(n, hq, hkv, d, d_idx, seed=n)
+    P, _, _ = bf.full_mass(x["q"], x["k"], oracle.default_scale(d))
+    tq = torch.tensor(qi, dtype=torch.float64, requires_grad=True)
+    tk = torch.tensor(ki, dtype=torch.float64, requires_grad=True)
+    T = (tq @ tk.T) / math.sqrt(d_idx)
+    mask = torch.tril(torch.ones(n, n, dtype=torch.bool))
+    logq = torch.log_softmax(T.masked_fill(~mask, float("-inf")), dim=-1)
+    Pt = torch.tensor(P)
+    pos = Pt > 0
+    terms = torch.where(pos, Pt * (torch.log(torch.where(pos, Pt, torch.ones_like(Pt)))
+                                   - torch.where(mask, logq, torch.zeros_like(logq))),
+                        torch.zeros_like(Pt))
+    kl = terms.sum(dim=1)
+    loss = kl.mean()
+    gq, gk = torch.autograd.grad(loss, (tq, tk))
+    kd = oracle.KLDistillOracle(OracleLayer(x["q"], x["k"], x["v"]), qi, ki).full()
+    np.testing.assert_allclose(kd["kl"], kl.detach().numpy(), rtol=1e-10, atol=1e-12)
+    assert abs(kd["loss"] - float(loss.detach())) <= 1e-12
+    np.testing.assert_allclose(kd["dq"], gq.numpy(), rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(kd["dk"], gk.numpy(), rtol=1e-9, atol=1e-13)
+
+
+def test_kl_distill_is_zero_when_the_student_is_the_teacher():
+    """One query head, one KV head, d_idx = d and the same temperature: the
+    student's distribution is the teacher's, so every KL and gradient is 0."""
+    n, d = 40, 16
+    x = random_inputs(n, 1, 1, d, "f32", seed=61, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    kd = oracle.KLDistillOracle(layer, x["q"][:, 0, :], x["k"][:, 0, :]).full()
+    assert np.max(np.abs(kd["kl"])) <= 1e-13
+    assert np.max(np.abs(kd["dq"])) <= 1e-15 and np.max(np.abs(kd["dk"])) <= 1e-15
+
+
+def test_kl_distill_invariances():
+    """KL >= 0; a vector u added to every k_idx row shifts each student row by
+    a constant, so the loss is unchanged and the key gradients sum to 0;
+    sum_i <q_i, dq_i> = sum_j <k_j, dk_j> (both are sum_ij dL/dt_ij t_ij)."""
+    n, d_idx = 50, 8
+    x, qi, ki = _kl_inputs(n, 8, 2, 16, d_idx, seed=67)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    a = oracle.KLDistillOracle(layer, qi, ki).full()
+    u = np.random.default_rng(3).standard_normal(d_idx)
+    b = oracle.KLDistillOracle(layer, qi, ki + u).full()
+    assert np.all(a["kl"] >= -1e-15)
+    np.testing.assert_allclose(a["kl"], b["kl"], rtol=1e-10, atol=1e-12)
+    assert np.max(np.abs(a["dk"].sum(axis=0))) <= 1e-12 * max(1.0, np.abs(a["dk"]).max() * n)
+    lhs = float(np.sum(qi.astype(np.float64) * a["dq"]))
+    rhs = float(np.sum(ki.astype(np.float64) * a["dk"]))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_kl_distill_row_and_key_subsets_match_the_full_pass():
+    n = 36
+    x, qi, ki = _kl_inputs(n, 4, 2, 8, 6, seed=71)
+    kd = oracle.KLDistillOracle(OracleLayer(x["q"], x["k"], x["v"]), qi, ki)
+    full = kd.full()
+    for i in (0, 7, 35):
+        assert abs(kd.row(i)["kl"] - full["kl"][i]) <= 1e-14
+        np.testing.assert_allclose(kd.dq(i), full["dq"][i], rtol=1e-12, atol=1e-16)
+    keys = [3, 20, 35]
+    np.testing.assert_allclose(kd.dk(keys), full["dk"][keys], rtol=1e-12, atol=1e-16)
+
+
 def test_needles_are_selected_on_tiny_workload():
     w = WORKLOADS["tiny_fp32_512"]
     x = generate(w)
