@@ -224,6 +224,37 @@ def diagnostics(amtk, w, x, k):
     return rep
 
 
+def kl_bench(amtk, w, x, steps, warmup):
+    """Times kl_distill (teacher LSE pass, student LSE pass, the KL tile
+    kernel with both gradients, the key-gradient reduction and the loss) on
+    the indexer workload's layer, inputs resident on the device."""
+    import torch
+    dev = torch.device("cuda:0")
+    t = {key: torch.from_numpy(x[key]).to(torch.bfloat16).to(dev)
+         for key in ("q", "k", "q_idx", "k_idx")}
+    ad = amtk.attn_desc(t["q"], t["k"])
+    ws = amtk.workspace(amtk.kl_workspace_bytes(ad, w.indexer_d), dev)
+    for _ in range(warmup):
+        amtk.kl_distill(t["q"], t["k"], t["q_idx"], t["k_idx"], ws=ws)
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        kl, loss, dq, dk = amtk.kl_distill(t["q"], t["k"], t["q_idx"], t["k_idx"], ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    n = w.n
+    pairs = n * (n + 1) // 2
+    # two teacher QK^T passes (LSE, then mass); student: LSE pass, t, dq, dk
+    flops = 2 * (2 * w.d * w.hq * pairs) + 4 * (2 * w.indexer_d * pairs)
+    return {"kl_distill": w.name, "n": n, "steps": steps, "ms_per_call": ms,
+            "tokens_per_s": n / (ms * 1e-3), "loss": float(loss.item()),
+            "algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
+            "workspace_bytes": ws.numel()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +266,8 @@ def main():
                     help="1: a support per query; 64: one support per block of 64 queries")
     ap.add_argument("--diagnostics", action="store_true",
                     help="only print the support diagnostics of the workload and exit")
+    ap.add_argument("--kl", action="store_true",
+                    help="only time the KL-distillation loss and gradients (indexer workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -269,6 +302,12 @@ def main():
     x = generate(w)
     if args.diagnostics:
         print(json.dumps(diagnostics(amtk, w, x, k)), flush=True)
+        return
+    if args.kl:
+        if not w.indexer_d:
+            print("bench.py: --kl needs an indexer workload (indexer_bf16_32k)", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(kl_bench(amtk, w, x, args.steps, args.warmup)), flush=True)
         return
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

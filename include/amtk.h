@@ -231,6 +231,33 @@ int support_overlap(int64_t n, int32_t max_a, const int32_t* idx_a, const int32_
                     int32_t max_b, const int32_t* idx_b, const int32_t* count_b,
                     int32_t* overlap, void* stream);
 
+/* Bytes of device workspace kl_distill needs for these shapes. */
+int amtk_kl_workspace(const amtk_attn_desc* attn, int32_t d_idx, size_t* bytes);
+
+/*
+ * kl_distill - KL-distillation loss of the head-collapsed indexer against the
+ * oracle's dense head-averaged attention mass, and its gradients.
+ * [TB 2.2]: the indexer is trained by KL divergence from the dense
+ * attention-mass distribution, the backbone frozen. Teacher P_i = head-averaged
+ * mass of (q, k) over keys j <= i; student Q_i = causal softmax over j <= i of
+ * t_ij = idx_scale * <q_idx[i], k_idx[j]> (idx_scale <= 0: 1/sqrt(d_idx)).
+ *   kl_row[i] = sum_j P_ij (log P_ij - log Q_ij)     (P_ij = 0 terms count 0)
+ *   loss      = (1/n) sum_i kl_row[i]
+ *   dq_idx[i] = dloss/dq_idx[i] = (idx_scale/n) sum_j (Q_ij - P_ij) k_idx[j]
+ *   dk_idx[j] = dloss/dk_idx[j] = (idx_scale/n) sum_{i>=j} (Q_ij - P_ij) q_idx[i]
+ * No n x n matrix is stored; both gradients are deterministic (fixed
+ * summation order).
+ * q, k      : as for topk_support; bf16, d = 128, hkv = 8, hq = 32 only.
+ * q_idx     : [n][d_idx] bf16 (device), k_idx: [n][d_idx] bf16; d_idx = 64.
+ * kl_row    : OUT [n] fp32.   loss: OUT [1] fp32, or NULL.
+ * dq_idx    : OUT [n][d_idx] fp32.   dk_idx: OUT [n][d_idx] fp32.
+ * ws        : device workspace of ws_bytes >= amtk_kl_workspace() (about
+ *             (n/32)^2 * 4 KiB: the per tile-pair key-gradient partials).
+ */
+int kl_distill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale, const void* q,
+               const void* k, const void* q_idx, const void* k_idx, float* kl_row, float* loss,
+               float* dq_idx, float* dk_idx, void* ws, size_t ws_bytes, void* stream);
+
 /* Message for an AMTK_* code. Never NULL. */
 const char* amtk_strerror(int code);
 

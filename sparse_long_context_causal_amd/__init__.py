@@ -13,6 +13,7 @@ Functions (names follow the C ABI):
   sparse_attn_blocks(q, k, v, idx, count, query_block=64) -> out, lse_sparse
   captured_mass(lse_dense, lse_support)        -> captured [N]
   support_overlap(idx_a, count_a, idx_b, count_b) -> overlap [N]
+  kl_distill(q, k, q_idx, k_idx)               -> kl_row, loss, dq_idx, dk_idx
   oracle_prefill(q, k, v, budget, key_block=1) -> out, idx, count, mass, lse
   indexer_topk(q_idx, k_idx, budget, key_block=64) -> idx, count, mass
 q: [N, Hq, d], k/v: [N, Hkv, d], bf16 or fp32 CUDA (HIP) tensors, contiguous.
@@ -214,6 +215,40 @@ def support_overlap(idx_a, count_a, idx_b, count_b, out=None):
     return out
 
 
+def kl_workspace_bytes(ad, d_idx: int) -> int:
+    nbytes = ctypes.c_size_t(0)
+    _call("amtk_kl_workspace", ctypes.byref(ad), int(d_idx), ctypes.byref(nbytes))
+    return nbytes.value
+
+
+def kl_distill(q, k, q_idx, k_idx, scale: Optional[float] = None,
+               idx_scale: Optional[float] = None, ws=None):
+    """KL-distillation loss of the indexer (q_idx, k_idx) against the dense
+    head-averaged mass of (q, k), with the gradients of the mean loss.
+    Returns (kl_row [N] fp32, loss [1] fp32, dq_idx [N,d_idx] fp32,
+    dk_idx [N,d_idx] fp32)."""
+    torch = _torch()
+    _check_dev(q, k, q_idx, k_idx)
+    if q_idx.dtype != torch.bfloat16 or k_idx.dtype != torch.bfloat16:
+        raise TypeError("q_idx and k_idx must be bfloat16")
+    n = q.shape[0]
+    if q_idx.dim() != 2 or q_idx.shape[0] != n or k_idx.shape != q_idx.shape:
+        raise ValueError("q_idx and k_idx must both be [N, d_idx]")
+    ad = attn_desc(q, k, scale)
+    d_idx = q_idx.shape[1]
+    if ws is None:
+        ws = workspace(kl_workspace_bytes(ad, d_idx), q.device)
+    dev = q.device
+    kl = torch.empty((n,), dtype=torch.float32, device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    dq = torch.empty((n, d_idx), dtype=torch.float32, device=dev)
+    dk = torch.empty((n, d_idx), dtype=torch.float32, device=dev)
+    _call("kl_distill", ctypes.byref(ad), int(d_idx), ctypes.c_float(idx_scale or 0.0), _ptr(q),
+          _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(kl), _ptr(loss), _ptr(dq), _ptr(dk), _ptr(ws),
+          ws.numel(), _stream(dev))
+    return kl, loss, dq, dk
+
+
 def oracle_prefill(q, k, v, budget: int, key_block: int = 1, scale: Optional[float] = None,
                    candidate_cap: int = 0, want_mass: bool = True, want_lse: bool = True,
                    ws=None, query_block: int = 1):
@@ -267,7 +302,8 @@ def pool_stats(ad: AttnDesc, sd: SupportDesc, ws, device=None):
 
 
 __all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_blocks", "oracle_prefill",
-           "indexer_topk", "captured_mass", "support_overlap",
+           "indexer_topk", "captured_mass", "support_overlap", "kl_distill",
+           "kl_workspace_bytes",
            "topk_workspace_bytes", "indexer_workspace_bytes", "workspace", "pool_stats",
            "attn_desc", "support_desc", "AmtkError", "AttnDesc", "SupportDesc"]
 

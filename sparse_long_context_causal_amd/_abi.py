@@ -41,6 +41,9 @@ SIGNATURES = {
     "sparse_attn": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_attn_blocks": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "captured_mass": (ctypes.c_int, [_I64, _I32, _P, _P, _P, _P]),
+    "amtk_kl_workspace": (ctypes.c_int, [_A, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "kl_distill": (ctypes.c_int, [_A, _I32, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
     "support_overlap": (ctypes.c_int, [_I64, _I32, _P, _P, _I32, _P, _P, _P, _P]),
     "oracle_prefill": (ctypes.c_int, [_A, _S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "amtk_indexer_workspace": (ctypes.c_int, [_I64, _I32, _I32, _S, ctypes.POINTER(_SZ)]),

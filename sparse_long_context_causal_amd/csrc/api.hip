@@ -317,6 +317,75 @@ int support_overlap(int64_t n, int32_t max_a, const int32_t* idx_a, const int32_
   return AMTK_OK;
 }
 
+namespace {
+
+struct KlLayout {
+  size_t lse, lse_t, zero, part, total;
+};
+
+KlLayout kl_layout(const LayerShape& s) {
+  KlLayout L;
+  size_t off = 0;
+  L.lse = off;    off = round_up(off + (size_t)s.hq * s.n * sizeof(float));
+  L.lse_t = off;  off = round_up(off + (size_t)s.n * sizeof(float));
+  L.zero = off;   off = round_up(off + sizeof(int));
+  L.part = off;   off = round_up(off + amtk::kl_partial_bytes(s.n));
+  L.total = off;
+  return L;
+}
+
+int kl_check(const amtk_attn_desc* attn, int32_t d_idx, LayerShape* s, LayerShape* si) {
+  int rc = check_attn(attn, s);
+  if (rc) return rc;
+  if (d_idx < 1) return AMTK_E_INVALID;
+  if (!amtk::kl_shape_supported(*s, d_idx)) return AMTK_E_UNSUPPORTED;
+  *si = *s;
+  si->hq = 1;
+  si->hkv = 1;
+  si->d = d_idx;
+  return AMTK_OK;
+}
+
+}  // namespace
+
+int amtk_kl_workspace(const amtk_attn_desc* attn, int32_t d_idx, size_t* bytes) {
+  LayerShape s, si;
+  int rc = kl_check(attn, d_idx, &s, &si);
+  if (rc) return rc;
+  if (!bytes) return AMTK_E_INVALID;
+  *bytes = kl_layout(s).total;
+  return AMTK_OK;
+}
+
+int kl_distill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale, const void* q,
+               const void* k, const void* q_idx, const void* k_idx, float* kl_row, float* loss,
+               float* dq_idx, float* dk_idx, void* ws, size_t ws_bytes, void* stream) {
+  LayerShape s, si;
+  int rc = kl_check(attn, d_idx, &s, &si);
+  if (rc) return rc;
+  if (std::isnan(idx_scale) || std::isinf(idx_scale)) return AMTK_E_INVALID;
+  if (!q || !k || !q_idx || !k_idx || !kl_row || !dq_idx || !dk_idx || !ws) return AMTK_E_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_idx, 16) || !aligned(k_idx, 16) ||
+      !aligned(kl_row, 4) || !aligned(dq_idx, 16) || !aligned(dk_idx, 16) || !aligned(ws, 256) ||
+      (loss && !aligned(loss, 4)))
+    return AMTK_E_INVALID;
+  const KlLayout L = kl_layout(s);
+  if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  float* lse = reinterpret_cast<float*>(w + L.lse);
+  float* lse_t = reinterpret_cast<float*>(w + L.lse_t);
+  int* zero = reinterpret_cast<int*>(w + L.zero);
+  si.scale = idx_scale > 0.f ? idx_scale : 1.0f / std::sqrt((float)d_idx);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = amtk::launch_pass1_lse(s, q, k, lse, zero, st);
+  if (e == hipSuccess) e = amtk::launch_pass1_lse(si, q_idx, k_idx, lse_t, zero, st);
+  if (e == hipSuccess)
+    e = amtk::launch_kl_distill(s, d_idx, si.scale, q, k, q_idx, k_idx, lse, lse_t, kl_row, loss,
+                                dq_idx, dk_idx, reinterpret_cast<float*>(w + L.part), st);
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
 const char* amtk_strerror(int code) {
   switch (code) {
     case AMTK_OK: return "success";

@@ -259,6 +259,29 @@ __device__ __forceinline__ void barrier_phase() {
   asm volatile("" ::: "memory");
 }
 
+// The wave's G query tiles as MFMA B operands (query row qrow, d half lane/32),
+// held in registers for a whole pass.
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_q_tiles(const T* __restrict__ Q, int qrow, int hq, int g,
+                                             int lane, uint4 (&qc)[G][KTile<T, D>::kChunks]) {
+  typedef KTile<T, D> KT;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4* src = reinterpret_cast<const uint4*>(Q + ((size_t)qrow * hq + g * G + h) * D +
+                                                      (lane >> 5) * (D / 2));
+#pragma unroll
+    for (int c = 0; c < KT::kChunks; ++c) qc[h][c] = src[c];
+  }
+}
+
+template <typename T, int NC>
+__device__ __forceinline__ void score_tile(f32x16& acc, const uint4 (&kc)[NC],
+                                           const uint4 (&qc)[NC]) {
+  acc = f32x16{};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ChunkMma<T>::mma(acc, kc[c], qc[c]);
+}
+
 // Row of key / query m inside a 32-row tile held by accumulator register r.
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 

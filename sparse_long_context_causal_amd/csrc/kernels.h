@@ -88,6 +88,18 @@ hipError_t launch_support_overlap(int n, int max_a, const int32_t* idx_a, const 
                                   int max_b, const int32_t* idx_b, const int32_t* count_b,
                                   int32_t* overlap, hipStream_t stream);
 
+// KL distillation of the indexer (q_idx, k_idx: [n][d_idx] bf16) against the
+// head-averaged mass of (q, k): per-row KL, the mean loss (if loss is not
+// null) and the gradients of the mean loss, given the dense per-head LSE
+// lse [hq][n] and the student's LSE lse_t [n]. dk_part: kl_partial_bytes(n)
+// of scratch. bf16, d = 128, 8 KV heads x 4 query heads, d_idx = 64.
+bool kl_shape_supported(const LayerShape& s, int d_idx);
+size_t kl_partial_bytes(int n);
+hipError_t launch_kl_distill(const LayerShape& s, int d_idx, float idx_scale, const void* q,
+                             const void* k, const void* q_idx, const void* k_idx,
+                             const float* lse, const float* lse_t, float* kl_row, float* loss,
+                             float* dq, float* dk, float* dk_part, hipStream_t stream);
+
 bool pass_shape_supported(const LayerShape& s);
 bool sparse_shape_supported(const LayerShape& s);
 

@@ -58,27 +58,6 @@ __device__ __forceinline__ int hist_count(const unsigned* words, int b) {
   return (int)((words[b >> 1] >> ((b & 1) * 16)) & 0xffffu);
 }
 
-template <typename T, int D, int G>
-__device__ __forceinline__ void load_q_tiles(const T* __restrict__ Q, int qrow, int hq, int g,
-                                             int lane, uint4 (&qc)[G][KTile<T, D>::kChunks]) {
-  typedef KTile<T, D> KT;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4* src = reinterpret_cast<const uint4*>(Q + ((size_t)qrow * hq + g * G + h) * D +
-                                                      (lane >> 5) * (D / 2));
-#pragma unroll
-    for (int c = 0; c < KT::kChunks; ++c) qc[h][c] = src[c];
-  }
-}
-
-template <typename T, int NC>
-__device__ __forceinline__ void score_tile(f32x16& acc, const uint4 (&kc)[NC],
-                                           const uint4 (&qc)[NC]) {
-  acc = f32x16{};
-#pragma unroll
-  for (int c = 0; c < NC; ++c) ChunkMma<T>::mma(acc, kc[c], qc[c]);
-}
-
 // ------------------------------------------------------------------ pass 1
 template <typename T, int D, int G>
 __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,

@@ -161,6 +161,26 @@ def test_diagnostics_validation(lib):
     assert lib.support_overlap(10, 4, FAKE, FAKE, 4, FAKE, FAKE, odd, None) == -1
 
 
+def test_kl_distill_validation(lib):
+    from sparse_long_context_causal_amd import _abi
+    a, _ = _descs()                                     # fp32, d = 64: not the kernel's shape
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_kl_workspace(ctypes.byref(a), 64, ctypes.byref(need)) == -2
+    b = _abi.AttnDesc(1000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    assert lib.amtk_kl_workspace(ctypes.byref(b), 32, ctypes.byref(need)) == -2
+    assert lib.amtk_kl_workspace(ctypes.byref(b), 0, ctypes.byref(need)) == -1
+    assert lib.amtk_kl_workspace(ctypes.byref(b), 64, ctypes.byref(need)) == 0
+    nt = (1000 + 31) // 32
+    assert need.value >= nt * (nt + 1) // 2 * 32 * 64 * 4 + 32 * 1000 * 4
+    f = lib.kl_distill
+    args = [FAKE] * 8
+    assert f(ctypes.byref(b), 64, 0.0, *args, FAKE, need.value - 1, None) == -3
+    assert f(ctypes.byref(b), 64, float("nan"), *args, FAKE, need.value, None) == -1
+    bad = list(args)
+    bad[4] = None                                       # kl_row
+    assert f(ctypes.byref(b), 64, 0.0, *bad, FAKE, need.value, None) == -1
+
+
 def test_indexer_validation(lib):
     _, s = _descs(kb=64, k=16)
     f = lib.indexer_topk
