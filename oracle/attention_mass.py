@@ -320,6 +320,36 @@ class IndexerOracle:
         self.k = np.asarray(k_idx, dtype=np.float64)
         self.scale = default_scale(self.q.shape[1]) if scale is None else float(scale)
 
+    def query_block(self, t: int, k: int, key_block: int, b_sel: int = 64) -> dict:
+        """The indexer's support shared by selection block t ([TB 2.1] b_sel,
+        realised with the indexer as in [TB 2.2]; [TB 2.3] names the cost of
+        such runtime sharing the realization gap).
+
+        READING (as for the oracle's selection blocks): unit u (a key block,
+        or a token when key_block = 1) scores the mean over the block's rows of
+        the indexer mass the row puts on u's keys up to itself; the top-k units
+        by (score descending, id ascending) among those the block's last row
+        sees are shared by every row, each row attending over their tokens
+        j <= i.
+
+        Keys: rows; score [units the last row sees]; units (ascending); kth;
+        support {i: token ids of the shared units clipped to j <= i}.
+        """
+        rows = query_block_rows(t, b_sel, self.q.shape[0])
+        last = rows[-1]
+        colmean = np.zeros(last + 1)
+        for i in rows:
+            s = self.scale * (self.k[: i + 1] @ self.q[i])
+            m = np.max(s)
+            colmean[: i + 1] += np.exp(s - (m + math.log(np.sum(np.exp(s - m)))))
+        colmean /= len(rows)
+        score = colmean if key_block == 1 else block_masses(colmean, key_block)
+        units = top_units(score, k)
+        support = {i: tokens_of_blocks(units, key_block, i) if key_block > 1 else units[units <= i]
+                   for i in rows}
+        return {"rows": rows, "score": score, "units": units, "kth": kth_score(score, k),
+                "support": support}
+
     def row(self, i: int, k: int, key_block: int) -> dict:
         s = self.scale * (self.k[: i + 1] @ self.q[i])
         m = np.max(s)

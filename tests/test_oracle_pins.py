@@ -416,6 +416,50 @@ def test_kl_distill_row_and_key_subsets_match_the_full_pass():
     np.testing.assert_allclose(kd.dk(keys), full["dk"][keys], rtol=1e-12, atol=1e-16)
 
 
+# ------------------------------------------- indexer, selection-block shared
+@pytest.mark.parametrize("n,kb,b_sel,kk", [(150, 16, 32, 3), (200, 1, 64, 9), (97, 8, 64, 5)])
+def test_indexer_query_blocks_against_brute_force(n, kb, b_sel, kk):
+    """The indexer's block-shared support against a full-tensor formulation:
+    masked [N, N] indexer softmax, column mean over the block's rows, sums
+    over aligned key blocks, one stable argsort; supports clipped to j <= i."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(n + kb)
+    qi = rng.standard_normal((n, 12)).astype(np.float32)
+    ki = rng.standard_normal((n, 12)).astype(np.float32)
+    ix = IndexerOracle(qi, ki)
+    T = (qi.astype(np.float64) @ ki.astype(np.float64).T) / math.sqrt(12)
+    T = np.where(np.tril(np.ones((n, n), dtype=bool)), T, -np.inf)
+    P = softmax(T, axis=1)
+    for t in range((n + b_sel - 1) // b_sel):
+        r = ix.query_block(t, kk, kb, b_sel)
+        rows = list(range(t * b_sel, min(n, (t + 1) * b_sel)))
+        assert list(r["rows"]) == rows
+        last = rows[-1]
+        col = P[rows, : last + 1].mean(axis=0)
+        nb = (last + 1 + kb - 1) // kb
+        score = np.array([col[b * kb:(b + 1) * kb].sum() for b in range(nb)])
+        np.testing.assert_allclose(r["score"], score, atol=1e-12, rtol=0)
+        order = np.argsort(-score, kind="stable")
+        units = np.sort(order[: min(kk, nb)])
+        assert r["units"].tolist() == units.tolist()
+        for i in rows:
+            toks = sorted(j for b in units for j in range(b * kb, min((b + 1) * kb, i + 1)))
+            assert r["support"][i].tolist() == toks
+
+
+def test_indexer_query_block_of_one_row_is_the_per_row_indexer():
+    rng = np.random.default_rng(4)
+    qi = rng.standard_normal((70, 8))
+    ki = rng.standard_normal((70, 8))
+    ix = IndexerOracle(qi, ki)
+    for i in (0, 5, 63, 64, 69):
+        a = ix.query_block(i, 3, 16, 1)
+        b = ix.row(i, 3, 16)
+        assert a["units"].tolist() == b["units"].tolist()
+        np.testing.assert_allclose(a["score"], b["score"], atol=1e-14, rtol=0)
+        assert a["support"][i].tolist() == b["support"].tolist()
+
+
 def test_needles_are_selected_on_tiny_workload():
     w = WORKLOADS["tiny_fp32_512"]
     x = generate(w)
