@@ -255,6 +255,57 @@ def kl_bench(amtk, w, x, steps, warmup):
             "workspace_bytes": ws.numel()}
 
 
+def realisation(amtk, w, x, steps, warmup):
+    """The indexer-driven sparse prefill three ways on the indexer workload:
+    per query (indexer_topk + sparse_attn), selection blocks of 64 as two
+    launches (indexer_topk + sparse_attn_blocks) and fused (indexer_prefill:
+    one kernel per block scores, selects and attends, after the indexer's
+    LSE pass); with the mean dense mass each support keeps (the layer-level
+    side of the realization gap)."""
+    import torch
+    dev = torch.device("cuda:0")
+    t = {key: torch.from_numpy(x[key]).to(torch.bfloat16).to(dev)
+         for key in ("q", "k", "v", "q_idx", "k_idx")}
+    k, kb = w.k, w.key_block
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / steps
+
+    def blocks_unfused():
+        idx, cnt, _ = amtk.indexer_topk(t["q_idx"], t["k_idx"], k, kb, query_block=64)
+        return amtk.sparse_attn_blocks(t["q"], t["k"], t["v"], idx, cnt, 64, key_block=kb)
+
+    ms = {
+        "per_query": timed(lambda: amtk.indexer_prefill(t["q"], t["k"], t["v"], t["q_idx"],
+                                                        t["k_idx"], k, kb)),
+        "blocks_of_64_unfused": timed(blocks_unfused),
+        "blocks_of_64_fused": timed(lambda: amtk.indexer_prefill(t["q"], t["k"], t["v"], t["q_idx"],
+                                                                 t["k_idx"], k, kb, query_block=64)),
+    }
+    # captured dense mass of each support
+    _, _, _, lse = amtk.topk_support(t["q"], t["k"], k, kb)
+    ip, cp, _ = amtk.indexer_topk(t["q_idx"], t["k_idx"], k, kb)
+    _, lse_p = amtk.sparse_attn(t["q"], t["k"], t["v"], ip, cp, kb, want_lse=True)
+    ib, cb, _ = amtk.indexer_topk(t["q_idx"], t["k_idx"], k, kb, query_block=64)
+    _, lse_b = amtk.sparse_attn_blocks(t["q"], t["k"], t["v"], ib, cb, 64, key_block=kb,
+                                       want_lse=True)
+    cap_p = float(amtk.captured_mass(lse, lse_p).to(torch.float64).mean().item())
+    cap_b = float(amtk.captured_mass(lse, lse_b).to(torch.float64).mean().item())
+    return {"realisation": w.name, "n": w.n, "k": k, "key_block": kb, "steps": steps,
+            "ms": ms, "tokens_per_s": {key: w.n / (v * 1e-3) for key, v in ms.items()},
+            "captured_mass": {"per_query": cap_p, "blocks_of_64": cap_b}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +319,9 @@ def main():
                     help="only print the support diagnostics of the workload and exit")
     ap.add_argument("--kl", action="store_true",
                     help="only time the KL-distillation loss and gradients (indexer workload)")
+    ap.add_argument("--realisation", action="store_true",
+                    help="only time the indexer path per query, in blocks of 64 and fused "
+                         "(indexer workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -302,6 +356,13 @@ def main():
     x = generate(w)
     if args.diagnostics:
         print(json.dumps(diagnostics(amtk, w, x, k)), flush=True)
+        return
+    if args.realisation:
+        if not w.indexer_d:
+            print("bench.py: --realisation needs an indexer workload (indexer_bf16_32k)",
+                  file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(realisation(amtk, w, x, args.steps, args.warmup)), flush=True)
         return
     if args.kl:
         if not w.indexer_d:

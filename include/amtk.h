@@ -151,13 +151,14 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
  * a block of query_block consecutive queries; each query i then attends
  * over the shared keys j <= i, softmax renormalised over them.
  * Block t holds rows t*query_block .. min((t+1)*query_block, n) - 1; its
- * support is idx[t*query_block][0..count[t*query_block]) (token ids, any
- * order, distinct), i.e. the first row of the block in the [n][max_units]
- * layout topk_support writes with sup->query_block = query_block. The other
- * rows' entries are not read. Per row, ids < 0, ids >= n and ids > i are
- * skipped; a row left with no key gets O = 0 and LSE = -inf. The result
- * equals sparse_attn (key_block = 1) when every row of a block holds the
- * block's support.
+ * support is idx[t*query_block][0..count[t*query_block]) (token ids, or
+ * key-block ids expanded to their 64 tokens when key_block = 64; any order,
+ * distinct), i.e. the first row of the block in the [n][max_units] layout
+ * topk_support / indexer_topk write with sup->query_block = query_block. The
+ * other rows' entries are not read. Per row, negative ids, tokens >= n and
+ * tokens > i are skipped; a row left with no key gets O = 0 and LSE = -inf.
+ * The result equals sparse_attn (same key_block) when every row of a block
+ * holds the block's support.
  * Shapes: bf16, d = 128, hkv = 8, hq = 32, query_block = 64; anything else
  * returns AMTK_E_UNSUPPORTED (sparse_attn covers it row by row).
  *
@@ -165,9 +166,10 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
  * o         : OUT [n][hq][d] fp32.
  * lse_sparse: OUT [hq][n] fp32 log-sum-exp over each row's keys, or NULL.
  */
-int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t query_block, int32_t max_units,
-                       const void* q, const void* k, const void* v, const int32_t* idx,
-                       const int32_t* count, float* o, float* lse_sparse, void* stream);
+int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t key_block, int32_t query_block,
+                       int32_t max_units, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const int32_t* count, float* o, float* lse_sparse,
+                       void* stream);
 
 /*
  * oracle_prefill - topk_support followed by sparse_attn on the same stream:
@@ -195,11 +197,40 @@ int amtk_indexer_workspace(int64_t n, int32_t d_idx, int32_t dtype,
  * q_idx, k_idx: [n][d_idx] device tensors, d_idx = 64 or 128.
  * scale <= 0 selects 1/sqrt(d_idx).
  * idx/count/mass/ws as in topk_support.
+ * sup->query_block = 64 ([TB 2.1] selection blocks, realised with the
+ * indexer): one support per block of 64 queries; a unit scores the mean over
+ * the block's rows of their P_idx on its keys up to the row, the top-k units
+ * among those the last row sees go into the index row of every query of the
+ * block (mass = the block score). key_block = 64 runs one kernel per block
+ * (bf16, d_idx = 64, k <= 1024, at most 2048 key blocks); key_block = 1 the
+ * column-sum path of topk_support.
  */
 int indexer_topk(int64_t n, int32_t d_idx, int32_t dtype, float scale,
                  const amtk_support_desc* sup, const void* q_idx, const void* k_idx,
                  int32_t* idx, int32_t* count, float* mass, void* ws, size_t ws_bytes,
                  void* stream);
+
+/*
+ * indexer_prefill - the indexer-driven sparse prefill of one layer: the
+ * indexer's support from (q_idx, k_idx), then attention of (q, k, v) on it.
+ * [TB 2.2] (indexer inference: score, select top-k, recompute attention on
+ * the chosen tokens); [TB 2.3], [Abstract] (runtime realisation: selection
+ * blocks and kernel fusion).
+ * sup->query_block = 1: the per-query realisation, indexer_topk then
+ * sparse_attn (key_block as given).
+ * sup->query_block = 64, key_block = 64: the fused realisation. After the
+ * indexer's LSE pass one kernel per block of 64 queries scores the key
+ * blocks, selects the shared top-k and attends over them for every KV head
+ * (bf16, d = 128, hkv = 8, hq = 32, d_idx = 64, k <= 1024).
+ * q_idx, k_idx: [n][d_idx], the layer's dtype. idx_scale <= 0: 1/sqrt(d_idx).
+ * o: OUT [n][hq][d] fp32; idx/count/mass: OUT, the support as indexer_topk
+ * writes it (mass may be NULL). ws: ws_bytes >= amtk_indexer_workspace(n,
+ * d_idx, dtype, sup).
+ */
+int indexer_prefill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale,
+                    const amtk_support_desc* sup, const void* q, const void* k, const void* v,
+                    const void* q_idx, const void* k_idx, float* o, int32_t* idx, int32_t* count,
+                    float* mass, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * captured_mass - per row, the head-averaged dense attention mass that a

@@ -16,6 +16,8 @@ Functions (names follow the C ABI):
   kl_distill(q, k, q_idx, k_idx)               -> kl_row, loss, dq_idx, dk_idx
   oracle_prefill(q, k, v, budget, key_block=1) -> out, idx, count, mass, lse
   indexer_topk(q_idx, k_idx, budget, key_block=64) -> idx, count, mass
+  indexer_prefill(q, k, v, q_idx, k_idx, budget, key_block=64, query_block=1)
+                                               -> out, idx, count, mass
 q: [N, Hq, d], k/v: [N, Hkv, d], bf16 or fp32 CUDA (HIP) tensors, contiguous.
 """
 import ctypes
@@ -156,7 +158,7 @@ def sparse_attn(q, k, v, idx, count, key_block: int = 1, scale: Optional[float] 
     return out, lse
 
 
-def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64,
+def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64, key_block: int = 1,
                        scale: Optional[float] = None, want_lse: bool = False, out=None):
     """Attention of each selection block of query_block rows on the support in
     the block's first row (rows skip ids after themselves). Returns
@@ -174,8 +176,9 @@ def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64,
     if out is None:
         out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((hq, n), dtype=torch.float32, device=q.device) if want_lse else None
-    _call("sparse_attn_blocks", ctypes.byref(ad), int(query_block), int(idx.shape[1]), _ptr(q),
-          _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _stream(q.device))
+    _call("sparse_attn_blocks", ctypes.byref(ad), int(key_block), int(query_block),
+          int(idx.shape[1]), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(out),
+          _ptr(lse), _stream(q.device))
     return out, lse
 
 
@@ -273,15 +276,16 @@ def oracle_prefill(q, k, v, budget: int, key_block: int = 1, scale: Optional[flo
 
 
 def indexer_topk(q_idx, k_idx, budget: int, key_block: int = 64, scale: Optional[float] = None,
-                 candidate_cap: int = 0, want_mass: bool = True, ws=None):
-    """Head-collapsed indexer top-k. Returns (idx [N,k], count [N], mass [N,k] or None)."""
+                 candidate_cap: int = 0, want_mass: bool = True, ws=None, query_block: int = 1):
+    """Head-collapsed indexer top-k. Returns (idx [N,k], count [N], mass [N,k] or None).
+    query_block = 64 shares one support among each block of 64 queries."""
     torch = _torch()
     _check_dev(q_idx, k_idx)
     if q_idx.dim() != 2 or q_idx.shape != k_idx.shape or q_idx.dtype != k_idx.dtype:
         raise ValueError("q_idx and k_idx must both be [N, d_idx] with one dtype")
     n, di = q_idx.shape
     code = _dtype_code(q_idx)
-    sd = support_desc(budget, key_block, candidate_cap)
+    sd = support_desc(budget, key_block, candidate_cap, query_block)
     if ws is None:
         ws = workspace(indexer_workspace_bytes(n, di, code, sd), q_idx.device)
     idx = torch.empty((n, budget), dtype=torch.int32, device=q_idx.device)
@@ -293,6 +297,37 @@ def indexer_topk(q_idx, k_idx, budget: int, key_block: int = 64, scale: Optional
     return idx, count, mass
 
 
+def indexer_prefill(q, k, v, q_idx, k_idx, budget: int, key_block: int = 64,
+                    query_block: int = 1, scale: Optional[float] = None,
+                    idx_scale: Optional[float] = None, want_mass: bool = True, ws=None, out=None):
+    """Indexer-driven sparse prefill: the indexer's support, then attention on
+    it. query_block = 1: per query (indexer_topk + sparse_attn); 64: the fused
+    realisation (one kernel per block of 64 queries scores, selects and
+    attends). Returns (out [N,Hq,d] fp32, idx, count, mass or None)."""
+    torch = _torch()
+    _check_dev(q, k, v, q_idx, k_idx)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    if q_idx.dim() != 2 or q_idx.shape != k_idx.shape or q_idx.dtype != q.dtype:
+        raise ValueError("q_idx and k_idx must both be [N, d_idx] in the layer's dtype")
+    ad = attn_desc(q, k, scale)
+    n, hq, d = q.shape
+    di = q_idx.shape[1]
+    sd = support_desc(budget, key_block, 0, query_block)
+    dev = q.device
+    if ws is None:
+        ws = workspace(indexer_workspace_bytes(n, di, _dtype_code(q_idx), sd), dev)
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((n, budget), dtype=torch.int32, device=dev)
+    count = torch.empty((n,), dtype=torch.int32, device=dev)
+    mass = torch.empty((n, budget), dtype=torch.float32, device=dev) if want_mass else None
+    _call("indexer_prefill", ctypes.byref(ad), int(di), ctypes.c_float(idx_scale or 0.0),
+          ctypes.byref(sd), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(out),
+          _ptr(idx), _ptr(count), _ptr(mass), _ptr(ws), ws.numel(), _stream(dev))
+    return out, idx, count, mass
+
+
 def pool_stats(ad: AttnDesc, sd: SupportDesc, ws, device=None):
     """(max candidates in a row, rows recomputed densely, capacity) of the last run on ws."""
     mx, ov, cap = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
@@ -302,7 +337,7 @@ def pool_stats(ad: AttnDesc, sd: SupportDesc, ws, device=None):
 
 
 __all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_blocks", "oracle_prefill",
-           "indexer_topk", "captured_mass", "support_overlap", "kl_distill",
+           "indexer_topk", "indexer_prefill", "captured_mass", "support_overlap", "kl_distill",
            "kl_workspace_bytes",
            "topk_workspace_bytes", "indexer_workspace_bytes", "workspace", "pool_stats",
            "attn_desc", "support_desc", "AmtkError", "AttnDesc", "SupportDesc"]
@@ -361,9 +396,9 @@ class PrefillPlan:
     def attn(self):
         qb = self.sd.query_block
         if qb != 1 and self.shared_tiles:
-            _call("sparse_attn_blocks", ctypes.byref(self.ad), qb, self.budget, _ptr(self.q),
-                  _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count), _ptr(self.out),
-                  None, _stream(self.q.device))
+            _call("sparse_attn_blocks", ctypes.byref(self.ad), self.key_block, qb, self.budget,
+                  _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count),
+                  _ptr(self.out), None, _stream(self.q.device))
             return
         _call("sparse_attn", ctypes.byref(self.ad), self.key_block, self.budget, _ptr(self.q),
               _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count), _ptr(self.out), None,

@@ -60,7 +60,6 @@ int check_support(const amtk_support_desc* sp) {
   if (sp->k > amtk::kMaxBudget) return AMTK_E_UNSUPPORTED;
   if (sp->key_block != 1 && sp->key_block != 64) return AMTK_E_UNSUPPORTED;
   if (sp->query_block != 1 && sp->query_block != kQueryBlock) return AMTK_E_UNSUPPORTED;
-  if (sp->query_block == kQueryBlock && sp->key_block != 1) return AMTK_E_UNSUPPORTED;
   return AMTK_OK;
 }
 
@@ -78,7 +77,10 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
     size_t off = 0;
     L.lse = off;     off = round_up(off + (size_t)s.hq * n * sizeof(float));
     L.ovf_count = off; off = round_up(off + sizeof(int));
-    L.colsum = off;  off = round_up(off + (n + 31) / 32 * n * sizeof(float));
+    // column sums per 32-row tile (token units only; key blocks are scored
+    // per selection block without them)
+    const size_t cs = sp.key_block == 1 ? (n + 31) / 32 * n * sizeof(float) : 0;
+    L.colsum = off;  off = round_up(off + cs);
     L.total = off;
     return L;
   }
@@ -121,6 +123,8 @@ int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const 
              const void* k, int32_t* idx, int32_t* count, float* mass, float* lse, void* ws,
              size_t ws_bytes, hipStream_t stream) {
   if (!amtk::pass_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  if (sp.query_block != 1 && sp.key_block != 1 && (s.hq != 1 || s.hkv != 1))
+    return AMTK_E_UNSUPPORTED;   // shared key blocks: the indexer's kernel only
   if (stage < 0 || stage > 3) return AMTK_E_INVALID;
   if (!q || !k || !ws || ((stage == 0 || stage == 3) && (!idx || !count))) return AMTK_E_INVALID;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
@@ -130,6 +134,20 @@ int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const 
   if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
   float* lse_buf = lse ? lse : reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + L.lse);
   hipError_t e = hipSuccess;
+  if (sp.query_block != 1 && sp.key_block != 1) {
+    // key blocks shared by a selection block: the indexer's per-block kernel
+    // (one head of d_idx, as indexer_topk passes it)
+    if (s.hq != 1 || s.hkv != 1 ||
+        !amtk::indexer_shared_supported(s.n, s.d, s.dtype, sp.key_block, sp.query_block, sp.k))
+      return AMTK_E_UNSUPPORTED;
+    int* zero = reinterpret_cast<int*>(static_cast<unsigned char*>(ws) + L.ovf_count);
+    if (stage == 0 || stage == 1) e = amtk::launch_pass1_lse(s, q, k, lse_buf, zero, stream);
+    if (e == hipSuccess && (stage == 0 || stage == 3))
+      e = amtk::launch_indexer_shared(s.n, sp.key_block, sp.k, s.scale, q, k, lse_buf, idx, count,
+                                      mass, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      stream);
+    return e == hipSuccess ? AMTK_OK : hip_fail(e);
+  }
   if (sp.query_block != 1) {   // one support per selection block of consecutive queries
     float* colsum = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + L.colsum);
     int* zero = reinterpret_cast<int*>(static_cast<unsigned char*>(ws) + L.ovf_count);
@@ -226,19 +244,21 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
   return AMTK_OK;
 }
 
-int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t query_block, int32_t max_units,
-                       const void* q, const void* k, const void* v, const int32_t* idx,
-                       const int32_t* count, float* o, float* lse_sparse, void* stream) {
+int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t key_block, int32_t query_block,
+                       int32_t max_units, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const int32_t* count, float* o, float* lse_sparse,
+                       void* stream) {
   LayerShape s;
   int rc = check_attn(attn, &s);
   if (rc) return rc;
   if (max_units < 1) return AMTK_E_INVALID;
+  if (key_block != 1 && key_block != 64) return AMTK_E_UNSUPPORTED;
   if (!amtk::shared_attn_shape_supported(s, query_block)) return AMTK_E_UNSUPPORTED;
   if (!q || !k || !v || !idx || !count || !o) return AMTK_E_INVALID;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
       !aligned(count, 4) || !aligned(o, 16) || (lse_sparse && !aligned(lse_sparse, 4)))
     return AMTK_E_INVALID;
-  hipError_t e = amtk::launch_shared_attn(s, query_block, max_units, q, k, v, idx, count, o,
+  hipError_t e = amtk::launch_shared_attn(s, key_block, query_block, max_units, q, k, v, idx, count, o,
                                           lse_sparse, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return AMTK_OK;
@@ -262,7 +282,8 @@ int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, con
   // gives the same result elsewhere
   hipError_t e =
       sup->query_block != 1 && amtk::shared_attn_shape_supported(s, sup->query_block)
-          ? amtk::launch_shared_attn(s, sup->query_block, sup->k, q, k, v, idx, count, o, nullptr, st)
+          ? amtk::launch_shared_attn(s, sup->key_block, sup->query_block, sup->k, q, k, v, idx, count,
+                                     o, nullptr, st)
           : amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o, nullptr, st);
   if (e != hipSuccess) return hip_fail(e);
   return AMTK_OK;
@@ -384,6 +405,47 @@ int kl_distill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale, const
                                 dq_idx, dk_idx, reinterpret_cast<float*>(w + L.part), st);
   if (e != hipSuccess) return hip_fail(e);
   return AMTK_OK;
+}
+
+int indexer_prefill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale,
+                    const amtk_support_desc* sup, const void* q, const void* k, const void* v,
+                    const void* q_idx, const void* k_idx, float* o, int32_t* idx, int32_t* count,
+                    float* mass, void* ws, size_t ws_bytes, void* stream) {
+  LayerShape s, si;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if ((rc = indexer_shape(s.n, d_idx, s.dtype, idx_scale, &si))) return rc;
+  if ((rc = check_support(sup))) return rc;
+  if (!amtk::sparse_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  if (!v || !o || !idx || !count) return AMTK_E_INVALID;
+  if (!aligned(v, 16) || !aligned(o, 16)) return AMTK_E_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (sup->query_block == 1) {   // per-query realisation: indexer_topk, then sparse_attn
+    rc = run_topk(si, *sup, 0, q_idx, k_idx, idx, count, mass, nullptr, ws, ws_bytes, st);
+    if (rc) return rc;
+    hipError_t e = amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o,
+                                            nullptr, st);
+    return e == hipSuccess ? AMTK_OK : hip_fail(e);
+  }
+  // fused realisation: the indexer's LSE pass, then one kernel per block of
+  // queries that scores, selects and attends
+  if (sup->key_block == 1 || !amtk::shared_attn_shape_supported(s, sup->query_block) ||
+      !amtk::indexer_shared_supported(si.n, si.d, si.dtype, sup->key_block, sup->query_block, sup->k))
+    return AMTK_E_UNSUPPORTED;
+  if (!q_idx || !k_idx || !q || !k || !ws) return AMTK_E_INVALID;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(idx, 4) || !aligned(count, 4) || !aligned(ws, 256) || (mass && !aligned(mass, 4)))
+    return AMTK_E_INVALID;
+  const Layout L = layout(si, *sup);
+  if (ws_bytes < L.total) return AMTK_E_WORKSPACE;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  float* lse_idx = reinterpret_cast<float*>(w + L.lse);
+  hipError_t e = amtk::launch_pass1_lse(si, q_idx, k_idx, lse_idx,
+                                        reinterpret_cast<int*>(w + L.ovf_count), st);
+  if (e == hipSuccess)
+    e = amtk::launch_indexer_shared(si.n, sup->key_block, sup->k, si.scale, q_idx, k_idx, lse_idx,
+                                    idx, count, mass, &s, q, k, v, o, nullptr, st);
+  return e == hipSuccess ? AMTK_OK : hip_fail(e);
 }
 
 const char* amtk_strerror(int code) {

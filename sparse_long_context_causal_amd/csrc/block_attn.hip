@@ -35,6 +35,7 @@
 //    about 16 significant bits (|p - hi - lo| <= 2^-16 p).
 #include "device_common.h"
 #include "kernels.h"
+#include "topk_core.h"
 
 namespace amtk {
 
@@ -46,6 +47,7 @@ constexpr int kBaWaves = 8;
 constexpr unsigned kBaTile = 8192;                       // 32 rows of 256 bytes
 constexpr unsigned kBaRowBytes = kBaHkv * kBaD * 2;      // one token, all KV heads
 constexpr unsigned kBaIdsOff = 4 * kBaTile;              // after K0, K1, V0, V1
+constexpr unsigned kBaLds = kBaIdsOff + 2 * 128;          // bytes of LDS a tile uses
 constexpr int kBaWaitVm0 = 0x0F70;                       // s_waitcnt vmcnt(0)
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -113,22 +115,25 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-__global__ __launch_bounds__(64 * kBaWaves) void shared_attn_mfma_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
-    float* __restrict__ lse_out, int n, int max_units, float c) {
-  __shared__ __align__(256) unsigned char smem[4 * kBaTile + 2 * 128];   // K0 K1 V0 V1, ids x2
+// One (selection block, KV head g) tile: wave w computes query head
+// 4g + (w & 3) for the queries i0 + 32(w >> 2) + [0, 32) over the support
+// units ids[0 .. cnt) (tokens, or KB-token key blocks), ids in global memory.
+// Every wave of the workgroup must call it with the same arguments; the
+// caller separates two calls on the same LDS with a barrier.
+template <int KB>
+__device__ __forceinline__ void shared_attn_tile(
+    unsigned char* __restrict__ smem, const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+    const bf16_t* __restrict__ V, const int32_t* __restrict__ ids, int cnt, int i0, int g,
+    float* __restrict__ O, float* __restrict__ lse_out, int n, float c) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int hl = lane >> 5;                       // half of the wave
-  const int t = (int)(blockIdx.x / kBaHkv), g = (int)(blockIdx.x % kBaHkv);
-  const int i0 = t * kBaRows;
   const int hh = kBaG * g + (w & 3);              // query head of this wave
   const int qrow = i0 + 32 * (w >> 2) + (lane & 31);
   const int qld = min(qrow, n - 1);
-  const int cnt = min(max(count[i0], 0), max_units);
-  const int nch = (cnt + 31) >> 5;
-  const int32_t* ids = idx + (size_t)i0 * max_units;
+  const int total = cnt * KB;                     // support tokens (before the causal clip)
+  const int nch = (total + 31) >> 5;
+  const int nunits = (n + KB - 1) / KB;
 
   const uint32_t base = lds_addr(smem);
   // DMA: lane 16q + m of wave w brings piece m of row R = 4w + q, which holds
@@ -139,9 +144,16 @@ __global__ __launch_bounds__(64 * kBaWaves) void shared_attn_mfma_kernel(
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K) + g * (kBaD * 2) + dx;
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V) + g * (kBaD * 2) + dx;
   const uint32_t dma_k = base + 1024u * (unsigned)w, dma_v = dma_k + 2 * kBaTile;
+  // token of the lane's DMA row in chunk ch (-1: padding or an invalid id)
   auto fetch_id = [&](int ch) -> int {
     const int slot = 32 * ch + (int)drow;
-    return slot < cnt ? ids[slot] : -1;
+    if (slot >= total) return -1;
+    if constexpr (KB == 1) {
+      return ids[slot];
+    } else {
+      const int b = ids[slot / KB];
+      return (b >= 0 && b < nunits) ? b * KB + slot % KB : -1;
+    }
   };
   // stage chunk ch: its ids (INT_MAX for padding and invalid ids) into the
   // ids buffer, then its key and value rows (row 0 stands in for an
@@ -155,7 +167,6 @@ __global__ __launch_bounds__(64 * kBaWaves) void shared_attn_mfma_kernel(
     __builtin_amdgcn_global_load_lds(Kb + off, (lds_ptr_t)(uintptr_t)(dma_k + kBaTile * b), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(Vb + off, (lds_ptr_t)(uintptr_t)(dma_v + kBaTile * b), 16, 0, 0);
   };
-
   // query fragment: B operand of k-step s, query lane%32, d = 16 s + 8 hl + [0, 8)
   u32x4 qf[8];
   {
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(64 * kBaWaves) void shared_attn_mfma_kernel(
     }
   }
   const float l = lrun + __shfl_xor(lrun, 32, 64);
-  if (qrow >= n) return;
+  if (qrow >= n) return;   // (no barrier follows inside the tile)
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   // O^T register r of tile dt: d = 32 dt + 8(r/4) + 4 hl + r%4
   float* op = O + ((size_t)qrow * kBaHq + hh) * kBaD + 4 * hl;
@@ -281,6 +292,137 @@ __global__ __launch_bounds__(64 * kBaWaves) void shared_attn_mfma_kernel(
     lse_out[(size_t)hh * n + qrow] = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
 }
 
+
+template <int KB>
+__global__ __launch_bounds__(64 * kBaWaves) void shared_attn_mfma_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
+    float* __restrict__ lse_out, int n, int max_units, float c) {
+  __shared__ __align__(256) unsigned char smem[kBaLds];
+  const int t = (int)(blockIdx.x / kBaHkv), g = (int)(blockIdx.x % kBaHkv);
+  const int i0 = t * kBaRows;
+  const int cnt = min(max(count[i0], 0), max_units);
+  shared_attn_tile<KB>(smem, Q, K, V, idx + (size_t)i0 * max_units, cnt, i0, g, O, lse_out, n, c);
+}
+
+// ---------------------------------------------------------------------------
+// The indexer's selection-block-shared support, and its fused realisation.
+// One workgroup (8 waves) per block of 64 queries:
+//  1. scores: unit u (KB tokens) gets the mean over the block's rows of the
+//     indexer mass P_idx_i(j) = exp(t_ij - LSE_idx(i)) summed over its keys
+//     j <= i. Wave w takes the units u = w (mod 8); per 32-key tile,
+//     S[query][key] = q_idx k_idx^T over the block's 64 queries is two
+//     32x32x16 MFMA tiles (A = the block's q_idx rows, held in registers;
+//     B = the tile's k_idx rows, loaded straight into registers), so lane l
+//     owns key l%32 and sums its 32 query registers, one xor-32 shuffle adds
+//     the other half, and a shuffle tree over the 32 keys gives the tile sum,
+//     all in a fixed order; the unit scores go to LDS;
+//  2. the block's top-k units with wg_topk, written (ascending) into the
+//     index row of every query of the block, with count and scores;
+//  3. fused realisation (kAttend): the block's attention tile for each KV
+//     head in turn (shared_attn_tile), reading the ids it just wrote.
+constexpr int kIxD = 64;             // indexer head dim
+constexpr int kIxMaxUnits = 2048;    // units a block's score row holds in LDS
+constexpr int kIxMaxK = 1024;        // winners held in LDS
+
+struct IndexerLds {
+  float score[kIxMaxUnits];
+  int win_id[kIxMaxK];
+  float win_m[kIxMaxK];
+  TopkScratch<512> sc;
+};
+
+template <int KB, bool kAttend>
+__global__ __launch_bounds__(512) void indexer_shared_kernel(
+    const bf16_t* __restrict__ QI, const bf16_t* __restrict__ KI, const float* __restrict__ lse_idx,
+    int n, int k, float ct, int32_t* __restrict__ idx, int32_t* __restrict__ count,
+    float* __restrict__ mass, const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+    const bf16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ lse_out, float c) {
+  static_assert(KB % 32 == 0, "units are whole 32-key tiles");
+  __shared__ __align__(256) unsigned char tile_lds[kAttend ? kBaLds : 16];
+  __shared__ IndexerLds ix;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hf = lane >> 5, col = lane & 31;
+  const int t = (int)blockIdx.x;
+  const int i0 = t * kBaRows, i1 = min(i0 + kBaRows, n) - 1;
+  const int nu = i1 / KB + 1;                  // units the block's last row sees
+  const float inv_rows = 1.0f / (float)(i1 - i0 + 1);
+
+  // ---- 1. unit scores
+  {
+    // A operands: the block's q_idx rows, query tile qt2 = 0, 1, k-step s
+    u32x4 qa[2][4];
+    float lse2[2][16];   // LSE_idx x log2e of the query in each accumulator register
+#pragma unroll
+    for (int qt2 = 0; qt2 < 2; ++qt2) {
+      const int qr = min(i0 + 32 * qt2 + col, n - 1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        qa[qt2][s] = *reinterpret_cast<const u32x4*>(QI + (size_t)qr * kIxD + 16 * s + 8 * hf);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = i0 + 32 * qt2 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        lse2[qt2][r] = qq < n ? lse_idx[qq] * kLog2e : INFINITY;   // rows past n weigh 0
+      }
+    }
+    for (int u = w; u < nu; u += 8) {
+      float usum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KB / 32; ++kt) {
+        const int k0 = u * KB + 32 * kt;
+        if (k0 > i1) break;
+        const int key = k0 + col;
+        const int kr = min(key, n - 1);
+        u32x4 kb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          kb[s] = *reinterpret_cast<const u32x4*>(KI + (size_t)kr * kIxD + 16 * s + 8 * hf);
+        float csum = 0.f;
+#pragma unroll
+        for (int qt2 = 0; qt2 < 2; ++qt2) {
+          f32x16 acc = f32x16{};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[qt2][s]),
+                                                          __builtin_bit_cast(bf16x8, kb[s]), acc, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qq = i0 + 32 * qt2 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const float p = fast_exp2(fmaf(acc[r], ct, -lse2[qt2][r]));
+            csum += (key <= qq) ? p : 0.f;
+          }
+        }
+        csum += __shfl_xor(csum, 32, 64);          // the other half's queries
+#pragma unroll
+        for (int sh = 1; sh < 32; sh <<= 1) csum += __shfl_xor(csum, sh, 64);
+        usum += csum;
+      }
+      if (lane == 0) ix.score[u] = usum * inv_rows;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. the block's top-k units
+  auto score = [&](int u) -> float { return ix.score[u]; };
+  const int kk = wg_topk<512>(score, nu, k, ix.sc, ix.win_id, ix.win_m);
+  for (int i = i0; i <= i1; ++i) {
+    for (int p = tid; p < k; p += 512) {
+      idx[(size_t)i * k + p] = p < kk ? ix.win_id[p] : -1;
+      if (mass) mass[(size_t)i * k + p] = p < kk ? ix.win_m[p] : 0.f;
+    }
+    if (tid == 0) count[i] = kk;
+  }
+
+  // ---- 3. the attention of the block's queries on the shared units
+  if constexpr (kAttend) {
+    __syncthreads();   // the block's index row is written (and visible to the workgroup)
+    for (int g = 0; g < kBaHkv; ++g) {
+      shared_attn_tile<KB>(tile_lds, Q, K, V, idx + (size_t)i0 * k, kk, i0, g, O, lse_out, n, c);
+      __syncthreads();   // the tile's LDS is free for the next head
+    }
+  }
+}
+
 }  // namespace
 
 bool shared_attn_shape_supported(const LayerShape& s, int query_block) {
@@ -288,16 +430,49 @@ bool shared_attn_shape_supported(const LayerShape& s, int query_block) {
          query_block == kBaRows;
 }
 
-hipError_t launch_shared_attn(const LayerShape& s, int query_block, int max_units, const void* q,
-                              const void* k, const void* v, const int32_t* idx,
+hipError_t launch_shared_attn(const LayerShape& s, int key_block, int query_block, int max_units,
+                              const void* q, const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream) {
-  if (!shared_attn_shape_supported(s, query_block)) return hipErrorInvalidValue;
+  if (!shared_attn_shape_supported(s, query_block) || (key_block != 1 && key_block != 64))
+    return hipErrorInvalidValue;
   const unsigned nblk = (unsigned)((s.n + kBaRows - 1) / kBaRows);
-  hipLaunchKernelGGL(shared_attn_mfma_kernel, dim3(nblk * kBaHkv), dim3(64 * kBaWaves), 0, stream,
+  auto kern = key_block == 1 ? shared_attn_mfma_kernel<1> : shared_attn_mfma_kernel<64>;
+  hipLaunchKernelGGL(kern, dim3(nblk * kBaHkv), dim3(64 * kBaWaves), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, max_units,
                      s.scale * kLog2e);
+  return hipGetLastError();
+}
+
+bool indexer_shared_supported(int n, int d_idx, int dtype, int key_block, int query_block,
+                              int budget) {
+  return dtype == kBF16 && d_idx == kIxD && key_block == 64 && query_block == kBaRows &&
+         (n + key_block - 1) / key_block <= kIxMaxUnits && budget <= kIxMaxK;
+}
+
+hipError_t launch_indexer_shared(int n, int key_block, int budget, float idx_scale,
+                                 const void* q_idx, const void* k_idx, const float* lse_idx,
+                                 int32_t* idx, int32_t* count, float* mass,
+                                 const LayerShape* attn, const void* q, const void* k,
+                                 const void* v, float* o, float* lse_sparse, hipStream_t stream) {
+  if (!indexer_shared_supported(n, kIxD, kBF16, key_block, kBaRows, budget))
+    return hipErrorInvalidValue;
+  const unsigned nblk = (unsigned)((n + kBaRows - 1) / kBaRows);
+  const float ct = idx_scale * kLog2e;
+  if (attn) {
+    if (!shared_attn_shape_supported(*attn, kBaRows) || attn->n != n) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((indexer_shared_kernel<64, true>), dim3(nblk), dim3(512), 0, stream,
+                       static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_idx),
+                       lse_idx, n, budget, ct, idx, count, mass, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), o, lse_sparse,
+                       attn->scale * kLog2e);
+  } else {
+    hipLaunchKernelGGL((indexer_shared_kernel<64, false>), dim3(nblk), dim3(512), 0, stream,
+                       static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_idx),
+                       lse_idx, n, budget, ct, idx, count, mass, nullptr, nullptr, nullptr,
+                       nullptr, nullptr, 0.f);
+  }
   return hipGetLastError();
 }
 

@@ -13,29 +13,25 @@
 // Input: pass 2's column sums over its 32-row tiles, colsum[t][j] = the sum
 // of P_i(j) over tile t's rows (written for keys j up to the tile's last
 // row). One workgroup per selection block forms the score row on the fly
-// from the block's tiles, finds the bit pattern of the k-th largest score
-// with a 4-pass radix select (scores are >= 0, so bit order is value order),
-// and emits the winners in id order in one ordered pass.
+// from the block's tiles and takes its top-k with wg_topk (radix select on
+// the score bits, winners emitted in id order).
 #include "device_common.h"
 #include "kernels.h"
+#include "topk_core.h"
 
 namespace amtk {
 
 constexpr int kBsThreads = 256;
-constexpr int kBsWaves = kBsThreads / 64;
 
 __global__ __launch_bounds__(kBsThreads) void block_topk_kernel(
     const float* __restrict__ colsum, int n, int bsel, int k, int32_t* __restrict__ idx,
     int32_t* __restrict__ count, float* __restrict__ mass) {
-  __shared__ unsigned hist[256];
-  __shared__ int scal[2];
-  __shared__ int wsum[2][kBsWaves];
+  __shared__ TopkScratch<kBsThreads> sc;
   extern __shared__ __align__(16) unsigned char dyn[];   // winners: ids [k], scores [k]
   int* win_id = reinterpret_cast<int*>(dyn);
   float* win_m = reinterpret_cast<float*>(dyn + (size_t)k * sizeof(int));
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const unsigned long long below = (1ull << l) - 1ull;
+  const int tid = threadIdx.x;
   const int i0 = (int)blockIdx.x * bsel, i1 = min(i0 + bsel, n) - 1;   // the block's rows
   const int nk = i1 + 1;                                                // keys its last row sees
   const float inv_rows = 1.0f / (float)(i1 - i0 + 1);
@@ -48,75 +44,7 @@ __global__ __launch_bounds__(kBsThreads) void block_topk_kernel(
     return acc * inv_rows;
   };
 
-  // the k-th largest score's bit pattern thr, and how many scores equal to
-  // it are taken (the rest of the k are above it); everything when nk <= k
-  const bool all = nk <= k;
-  unsigned thr = 0u;
-  int take = 0;
-  if (!all) {
-    unsigned prefix = 0u, pmask = 0u;
-    int rem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = tid; b < 256; b += kBsThreads) hist[b] = 0u;
-      __syncthreads();
-      for (int j = tid; j < nk; j += kBsThreads) {
-        const unsigned v = __float_as_uint(score(j));
-        if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int acc = 0, d = 255;
-        for (; d > 0; --d) {
-          if (acc + (int)hist[d] >= rem) break;
-          acc += (int)hist[d];
-        }
-        scal[0] = d;
-        scal[1] = rem - acc;
-      }
-      __syncthreads();
-      prefix |= (unsigned)scal[0] << shift;
-      pmask |= 255u << shift;
-      rem = scal[1];
-      __syncthreads();
-    }
-    thr = prefix;
-    take = rem;
-  }
-
-  // ordered emission: keys above thr, and the first `take` equal to it
-  int base = 0, eq_seen = 0;
-  for (int j0 = 0; j0 < nk; j0 += kBsThreads) {
-    const int j = j0 + tid;
-    float m = 0.f;
-    bool gt = false, eq = false;
-    if (j < nk) {
-      m = score(j);
-      const unsigned v = __float_as_uint(m);
-      gt = all || v > thr;
-      eq = !all && v == thr;
-    }
-    const unsigned long long be = __ballot(eq);
-    if (l == 0) wsum[0][w] = __popcll(be);
-    __syncthreads();
-    int eq_before = eq_seen + __popcll(be & below);
-    for (int ww = 0; ww < w; ++ww) eq_before += wsum[0][ww];
-    const bool keep = gt || (eq && eq_before < take);
-    const unsigned long long bk = __ballot(keep);
-    if (l == 0) wsum[1][w] = __popcll(bk);
-    __syncthreads();
-    int pos = base + __popcll(bk & below);
-    for (int ww = 0; ww < w; ++ww) pos += wsum[1][ww];
-    if (keep && pos < k) {   // (pos < k always holds: at most k scores are kept)
-      win_id[pos] = j;
-      win_m[pos] = m;
-    }
-    for (int ww = 0; ww < kBsWaves; ++ww) {
-      eq_seen += wsum[0][ww];
-      base += wsum[1][ww];
-    }
-    __syncthreads();
-  }
-  const int kk = base;   // = min(k, nk)
+  const int kk = wg_topk<kBsThreads>(score, nk, k, sc, win_id, win_m);
 
   for (int i = i0; i <= i1; ++i) {
     for (int p = tid; p < k; p += kBsThreads) {

@@ -73,11 +73,24 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
 // support: the ids and count of the block's first row serve all of its rows,
 // each row skipping the ids after it. bf16, d = 128, 8 KV heads x 4 query
 // heads, blocks of 64 queries (shared_attn_shape_supported).
-hipError_t launch_shared_attn(const LayerShape& s, int query_block, int max_units, const void* q,
-                              const void* k, const void* v, const int32_t* idx,
+hipError_t launch_shared_attn(const LayerShape& s, int key_block, int query_block, int max_units,
+                              const void* q, const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream);
 bool shared_attn_shape_supported(const LayerShape& s, int query_block);
+
+// The indexer's support shared by each block of 64 queries (key blocks of
+// 64): scores and top-k in one kernel per block, given the indexer's row LSE
+// lse_idx [n]. With attn (q, k, v, o, lse_sparse) the same kernel then runs
+// the block's attention on the shared keys for every KV head (the fused
+// realisation); attn = nullptr selects only.
+bool indexer_shared_supported(int n, int d_idx, int dtype, int key_block, int query_block,
+                              int budget);
+hipError_t launch_indexer_shared(int n, int key_block, int budget, float idx_scale,
+                                 const void* q_idx, const void* k_idx, const float* lse_idx,
+                                 int32_t* idx, int32_t* count, float* mass,
+                                 const LayerShape* attn, const void* q, const void* k,
+                                 const void* v, float* o, float* lse_sparse, hipStream_t stream);
 
 // Diagnostics: captured[i] = (1/hq) sum_h exp(lse_support[h][i] - lse_dense[h][i])
 // (-inf support LSE counts 0); overlap[i] = ids shared by two supports whose

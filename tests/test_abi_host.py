@@ -138,15 +138,39 @@ def test_sparse_attn_validation(lib):
 def test_sparse_attn_blocks_validation(lib):
     f = lib.sparse_attn_blocks
     a, _ = _descs()
-    assert f(ctypes.byref(a), 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(ctypes.byref(a), 1, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
     # the tile kernel's shape only: bf16, d = 128, 8 KV x 4 query heads, blocks of 64
-    assert f(ctypes.byref(a), 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert f(ctypes.byref(a), 1, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
     from sparse_long_context_causal_amd import _abi
     b = _abi.AttnDesc(1000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
-    assert f(ctypes.byref(b), 32, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
-    assert f(ctypes.byref(b), 64, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(ctypes.byref(b), 1, 32, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert f(ctypes.byref(b), 16, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert f(ctypes.byref(b), 64, 64, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
     odd = ctypes.c_void_p(0x100004)   # o must be 16-byte aligned
-    assert f(ctypes.byref(b), 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, odd, None, None) == -1
+    assert f(ctypes.byref(b), 1, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, odd, None, None) == -1
+
+
+def test_indexer_prefill_validation(lib):
+    from sparse_long_context_causal_amd import _abi
+    f = lib.indexer_prefill
+    b = _abi.AttnDesc(1000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    s_fused = _abi.SupportDesc(16, 64, 64, 0)
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_indexer_workspace(1000, 64, _abi.AMTK_BF16, ctypes.byref(s_fused),
+                                      ctypes.byref(need)) == 0
+    args = [FAKE] * 5                                   # q, k, v, q_idx, k_idx
+    outs = [FAKE, FAKE, FAKE, None]                     # o, idx, count, mass
+    ok = lambda sd, **kw: f(ctypes.byref(kw.get("a", b)), kw.get("di", 64), 0.0, ctypes.byref(sd),
+                            *kw.get("args", args), *kw.get("outs", outs), FAKE,
+                            kw.get("ws", need.value), None)
+    assert ok(s_fused, ws=need.value - 1) == -3
+    assert ok(s_fused, di=32) == -2                     # the fused kernel wants d_idx = 64
+    assert ok(_abi.SupportDesc(16, 1, 64, 0)) == -2     # fused: key blocks of 64 only
+    assert ok(_abi.SupportDesc(2000, 64, 64, 0)) == -2  # more winners than its LDS holds
+    a, _ = _descs()
+    assert ok(s_fused, a=a) == -2                       # not the tile kernel's layer shape
+    assert ok(s_fused, outs=[None, FAKE, FAKE, None]) == -1
+    assert ok(s_fused, args=[FAKE, FAKE, FAKE, None, FAKE]) == -1
 
 
 def test_diagnostics_validation(lib):
