@@ -45,6 +45,19 @@
 
 namespace amtk {
 
+// Column-sum mode: tiles of per-wave key sums held in LDS before a fold.
+constexpr int kCsRing = 32;
+
+// DPP lane permutations within rows of 16 lanes
+constexpr int kDppRowMirror = 0x140;       // lane i <-> 15 - i
+constexpr int kDppRowHalfMirror = 0x141;   // lane i <-> 7 - i within each 8
+constexpr int kDppQuadXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;         // quad_perm [1,0,3,2]
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 // Mass bins of the filter (kFBins, 8 per octave), u16 counts packed two
 // per LDS word.
 constexpr int kFBinWords = kFBins / 2;
@@ -479,34 +492,57 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     float pacc[16];
     tile_mass(diag, pacc);
 
+    if constexpr (CS) {
+      // ---- column sums: each wave sums its heads' masses over the tile's
+      // rows in registers (a reduce-scatter over the 32 query lanes of each
+      // half: one xor-16 exchange, then DPP row mirror, half mirror, xor 2,
+      // xor 1), leaving the sum of key 16 b4 + 8 b3 + 4 hf + 2 b2 + b1 (lane
+      // bits b) in lanes l and l^1; the 8 waves' sums go to an LDS ring of
+      // kCsRing tiles that the workgroup folds (fixed order) and stores every
+      // kCsRing tiles, so there is no barrier per tile.
+      if (q0 + col >= n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] = 0.f;   // rows past n
+      }
+      const bool u16 = lane & 16, u8 = lane & 8, u4 = lane & 4, u2 = lane & 2;
+      float v8[8], v4[4], v2[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v8[i] = (u16 ? pacc[i + 8] : pacc[i]) + __shfl_xor(u16 ? pacc[i] : pacc[i + 8], 16, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v4[i] = (u8 ? v8[i + 4] : v8[i]) + dpp_f32<kDppRowMirror>(u8 ? v8[i] : v8[i + 4]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        v2[i] = (u4 ? v4[i + 2] : v4[i]) + dpp_f32<kDppRowHalfMirror>(u4 ? v4[i] : v4[i + 2]);
+      float v1 = (u2 ? v2[1] : v2[0]) + dpp_f32<kDppQuadXor2>(u2 ? v2[0] : v2[1]);
+      v1 += dpp_f32<kDppQuadXor1>(v1);
+      const int slot = kt % kCsRing;
+      if ((lane & 1) == 0) {
+        const int key = 16 * (int)u16 + 8 * (int)u8 + 4 * hf + 2 * (int)u4 + (int)u2;
+        part[(slot * hkv + g) * 32 + key] = v1;
+      }
+      if (slot == kCsRing - 1 || diag) {
+        barrier_lds();   // the ring's tiles are complete
+        const int kt0 = kt - slot;
+        for (int e = (int)threadIdx.x; e < (slot + 1) * 32; e += nthreads) {
+          const int sl = e >> 5, key = e & 31;
+          const float* src = part + sl * hkv * 32 + key;
+          float sum = src[0];
+          for (int gg = 1; gg < hkv; ++gg) sum += src[gg * 32];
+          const int j = ((kt0 + sl) << 5) + key;
+          if (j < n) colsum[(size_t)qt * n + j] = sum * inv_hq;
+        }
+        barrier_lds();   // the ring is free again
+      }
+      continue;
+    }
     if constexpr (KB == 1) {
       float* pb = part + (kt & 1) * part_floats;
       const int wb = (kt & 1) * part_floats + g * 1024 + lane;   // = part_index(g, 0, lane) in this buffer
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[wb ^ (68 * r)] = pacc[r];
       barrier_lds();   // partial masses visible
-      if constexpr (CS) {
-        // ---- column sums: sum over the tile's rows i < n of P_i(j) for each
-        // of its 32 keys (2*hkv threads per key, 16/hkv rows each; the causal
-        // zeros of the diagonal tile are already in the partials), summed in
-        // a fixed order
-        const float* pb = part + (kt & 1) * part_floats;
-        const int tpk = 2 * hkv, key = (int)threadIdx.x / tpk, j0 = (int)threadIdx.x % tpk;
-        const int r = ((key >> 3) << 2) | (key & 3), h2 = (key >> 2) & 1;
-        float sum = 0.f;
-        for (int e = 0; e < 16 / hkv; ++e) {
-          const int qq = j0 + tpk * e;
-          if (q0 + qq < n) {
-            const float* src = pb + part_index(0, r, qq + 32 * h2);
-            float p = src[0];
-            for (int gg = 1; gg < hkv; ++gg) p += src[gg * 16 * 64];
-            sum += p;
-          }
-        }
-        for (int sh = 1; sh < tpk; sh <<= 1) sum += __shfl_xor(sum, sh, 64);
-        if (j0 == 0 && k0 + key < n) colsum[(size_t)qt * n + k0 + key] = sum * inv_hq;
-        continue;
-      }
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       // A mass passes the bound bin exactly when its bit pattern is at least
       // the bin's floor pattern, so the bin itself is only formed for the
