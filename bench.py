@@ -340,7 +340,7 @@ def main():
                           "bytes_written": nbytes}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); the "
               "path shards by query rows across GPUs, which is not built here.", file=sys.stderr)
         sys.exit(2)
 
