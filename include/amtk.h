@@ -144,6 +144,31 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
                 const void* k, const void* v, const int32_t* idx, const int32_t* count, float* o,
                 float* lse_sparse, void* stream);
 
+/* Scratch bytes of sparse_attn_windowed for this layer shape. */
+int amtk_sparse_attn_workspace(const amtk_attn_desc* attn, size_t* bytes);
+
+/*
+ * sparse_attn_windowed - sparse_attn computed in key windows: the same
+ * result (up to fp32 rounding order) with better cache reuse at long n.
+ * [TB 2.1], [TB 2.2], [Abstract], as sparse_attn. The supports are walked
+ * in windows of at least 8192 consecutive key tokens, one launch per
+ * window; each launch attends every row over its ids in that window and
+ * merges the partial softmax into o (o stays normalised; the running LSE
+ * lives in lse_sparse when given, else in ws). Rows whose ids are ascending
+ * (as topk_support writes them) are split this way; a row whose ids are not
+ * ascending is attended whole in the first window. Where the windowed form
+ * does not apply (other shapes than bf16, d = 128, hkv = 8, hq = 32; n of
+ * one window) the call is sparse_attn.
+ *
+ * Arguments as sparse_attn, plus ws: device scratch of ws_bytes >=
+ * amtk_sparse_attn_workspace bytes, 256-byte aligned, owned by the caller
+ * (AMTK_E_WORKSPACE if smaller). Its contents on return are unspecified.
+ */
+int sparse_attn_windowed(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units,
+                         const void* q, const void* k, const void* v, const int32_t* idx,
+                         const int32_t* count, float* o, float* lse_sparse, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /*
  * sparse_attn_blocks - attention of each selection block's queries on the
  * block's shared support, the keys gathered once per block.
@@ -177,7 +202,10 @@ int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t key_block, int32_t qu
  * recompute with the original Q/K/V), [TB 2.1], [Abstract].
  * Arguments as in the two calls above; idx and count are required outputs.
  * With sup->query_block = 64 the sparse step is sparse_attn_blocks where it
- * supports the shape, else sparse_attn on the per-row copies.
+ * supports the shape, else sparse_attn on the per-row copies. With
+ * query_block = 1 it is sparse_attn_windowed, its scratch taken from the
+ * candidate pool of ws (free once the supports are selected) when the pool
+ * is large enough, else sparse_attn.
  */
 int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
                    const void* k, const void* v, float* o, int32_t* idx, int32_t* count,

@@ -158,6 +158,39 @@ def sparse_attn(q, k, v, idx, count, key_block: int = 1, scale: Optional[float] 
     return out, lse
 
 
+def sparse_attn_workspace_bytes(ad) -> int:
+    """Scratch bytes of sparse_attn_windowed for the layer shape in ad."""
+    nbytes = ctypes.c_size_t(0)
+    _call("amtk_sparse_attn_workspace", ctypes.byref(ad), ctypes.byref(nbytes))
+    return int(nbytes.value)
+
+
+def sparse_attn_windowed(q, k, v, idx, count, key_block: int = 1, scale: Optional[float] = None,
+                         want_lse: bool = False, out=None, ws=None):
+    """sparse_attn walked in key windows (better cache reuse at long N; the
+    same result up to rounding order). Returns (out [N,Hq,d] fp32,
+    lse_sparse [Hq,N] or None)."""
+    torch = _torch()
+    _check_dev(q, k, v, idx, count)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    if idx.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("idx and count must be int32")
+    ad = attn_desc(q, k, scale)
+    n, hq, d = q.shape
+    if idx.dim() != 2 or idx.shape[0] != n or count.shape != (n,):
+        raise ValueError("idx must be [N, max_units] and count [N]")
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(sparse_attn_workspace_bytes(ad), q.device)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=q.device) if want_lse else None
+    _call("sparse_attn_windowed", ctypes.byref(ad), int(key_block), int(idx.shape[1]), _ptr(q),
+          _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+          _stream(q.device))
+    return out, lse
+
+
 def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64, key_block: int = 1,
                        scale: Optional[float] = None, want_lse: bool = False, out=None):
     """Attention of each selection block of query_block rows on the support in
@@ -336,7 +369,8 @@ def pool_stats(ad: AttnDesc, sd: SupportDesc, ws, device=None):
     return mx.value, ov.value, cap.value
 
 
-__all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_blocks", "oracle_prefill",
+__all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_windowed", "sparse_attn_blocks",
+           "sparse_attn_workspace_bytes", "oracle_prefill",
            "indexer_topk", "indexer_prefill", "captured_mass", "support_overlap", "kl_distill",
            "kl_workspace_bytes",
            "topk_workspace_bytes", "indexer_workspace_bytes", "workspace", "pool_stats",
@@ -346,14 +380,15 @@ __all__ = ["load", "topk_support", "sparse_attn", "sparse_attn_blocks", "oracle_
 class PrefillPlan:
     """Preallocated outputs + workspace for repeated oracle prefills of one layer shape.
 
-    run() enqueues topk_support stages 1-3 and sparse_attn on the current
-    stream; stage(s) / attn() enqueue one piece (for timing). The indexer
-    variant (indexer=True) runs indexer_topk on (q_idx, k_idx) instead of
-    topk_support, then sparse_attn over 64-token key blocks.
+    run() enqueues topk_support stages 1-3 and the gather (sparse_attn_windowed,
+    or sparse_attn with windowed=False; sparse_attn_blocks for selection
+    blocks) on the current stream; stage(s) / attn() enqueue one piece (for
+    timing). The indexer variant (q_idx, k_idx given) runs indexer_topk
+    instead of topk_support, then the gather over 64-token key blocks.
     """
 
     def __init__(self, q, k, v, budget, key_block=1, q_idx=None, k_idx=None, candidate_cap=0,
-                 query_block=1):
+                 query_block=1, windowed=True):
         torch = _torch()
         _check_dev(q, k, v)
         self.q, self.k, self.v = q, k, v
@@ -370,6 +405,10 @@ class PrefillPlan:
         else:
             nbytes = topk_workspace_bytes(self.ad, self.sd)
         self.ws = workspace(nbytes, dev)
+        # the per-row gather runs in key windows (sparse_attn_windowed) unless
+        # windowed=False asks for the one-pass sparse_attn
+        self.windowed = windowed
+        self.attn_ws = workspace(sparse_attn_workspace_bytes(self.ad), dev) if windowed else None
         self.idx = torch.empty((self.n, budget), dtype=torch.int32, device=dev)
         self.count = torch.empty((self.n,), dtype=torch.int32, device=dev)
         self.mass = torch.empty((self.n, budget), dtype=torch.float32, device=dev)
@@ -399,6 +438,12 @@ class PrefillPlan:
             _call("sparse_attn_blocks", ctypes.byref(self.ad), self.key_block, qb, self.budget,
                   _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count),
                   _ptr(self.out), None, _stream(self.q.device))
+            return
+        if self.windowed:
+            _call("sparse_attn_windowed", ctypes.byref(self.ad), self.key_block, self.budget,
+                  _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count),
+                  _ptr(self.out), None, _ptr(self.attn_ws), self.attn_ws.numel(),
+                  _stream(self.q.device))
             return
         _call("sparse_attn", ctypes.byref(self.ad), self.key_block, self.budget, _ptr(self.q),
               _ptr(self.k), _ptr(self.v), _ptr(self.idx), _ptr(self.count), _ptr(self.out), None,

@@ -40,6 +40,9 @@ SIGNATURES = {
     "topk_support_stage": (ctypes.c_int, [_A, _S, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparse_attn": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sparse_attn_blocks": (ctypes.c_int, [_A, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "amtk_sparse_attn_workspace": (ctypes.c_int, [_A, ctypes.POINTER(_SZ)]),
+    "sparse_attn_windowed": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                            _P]),
     "indexer_prefill": (ctypes.c_int, [_A, _I32, ctypes.c_float, _S, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "captured_mass": (ctypes.c_int, [_I64, _I32, _P, _P, _P, _P]),

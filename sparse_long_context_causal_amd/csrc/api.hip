@@ -244,6 +244,38 @@ int sparse_attn(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units
   return AMTK_OK;
 }
 
+int amtk_sparse_attn_workspace(const amtk_attn_desc* attn, size_t* bytes) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if (!bytes) return AMTK_E_INVALID;
+  *bytes = amtk::sparse_windowed_scratch_bytes(s);
+  return AMTK_OK;
+}
+
+int sparse_attn_windowed(const amtk_attn_desc* attn, int32_t key_block, int32_t max_units,
+                         const void* q, const void* k, const void* v, const int32_t* idx,
+                         const int32_t* count, float* o, float* lse_sparse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  LayerShape s;
+  int rc = check_attn(attn, &s);
+  if (rc) return rc;
+  if (max_units < 1) return AMTK_E_INVALID;
+  if (key_block != 1 && key_block != 64) return AMTK_E_UNSUPPORTED;
+  if (!amtk::sparse_shape_supported(s)) return AMTK_E_UNSUPPORTED;
+  if (!q || !k || !v || !idx || !count || !o || !ws) return AMTK_E_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
+      !aligned(count, 4) || !aligned(o, 16) || (lse_sparse && !aligned(lse_sparse, 4)) ||
+      !aligned(ws, 256))
+    return AMTK_E_INVALID;
+  if (ws_bytes < amtk::sparse_windowed_scratch_bytes(s)) return AMTK_E_WORKSPACE;
+  hipError_t e = amtk::launch_sparse_attn_windowed(s, key_block, max_units, q, k, v, idx, count, o,
+                                                   lse_sparse, ws, ws_bytes,
+                                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return AMTK_OK;
+}
+
 int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t key_block, int32_t query_block,
                        int32_t max_units, const void* q, const void* k, const void* v,
                        const int32_t* idx, const int32_t* count, float* o, float* lse_sparse,
@@ -280,11 +312,20 @@ int oracle_prefill(const amtk_attn_desc* attn, const amtk_support_desc* sup, con
   // selection blocks: one gather per block where the tile kernel covers the
   // shape; every row also holds its block's support, so the per-row kernel
   // gives the same result elsewhere
-  hipError_t e =
-      sup->query_block != 1 && amtk::shared_attn_shape_supported(s, sup->query_block)
-          ? amtk::launch_shared_attn(s, sup->key_block, sup->query_block, sup->k, q, k, v, idx, count,
-                                     o, nullptr, st)
-          : amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o, nullptr, st);
+  hipError_t e;
+  if (sup->query_block != 1) {
+    e = amtk::shared_attn_shape_supported(s, sup->query_block)
+            ? amtk::launch_shared_attn(s, sup->key_block, sup->query_block, sup->k, q, k, v, idx,
+                                       count, o, nullptr, st)
+            : amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o, nullptr, st);
+  } else {
+    // the candidate pool is free once the supports are selected: the
+    // windowed gather's scratch (it falls back to one pass if too small)
+    const Layout L = layout(s, *sup);
+    e = amtk::launch_sparse_attn_windowed(s, sup->key_block, sup->k, q, k, v, idx, count, o,
+                                          nullptr, static_cast<unsigned char*>(ws) + L.cand,
+                                          L.count - L.cand, st);
+  }
   if (e != hipSuccess) return hip_fail(e);
   return AMTK_OK;
 }
@@ -423,8 +464,13 @@ int indexer_prefill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale,
   if (sup->query_block == 1) {   // per-query realisation: indexer_topk, then sparse_attn
     rc = run_topk(si, *sup, 0, q_idx, k_idx, idx, count, mass, nullptr, ws, ws_bytes, st);
     if (rc) return rc;
-    hipError_t e = amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o,
-                                            nullptr, st);
+    // the indexer's candidate pool is free now: the windowed gather's
+    // scratch (one pass if it is too small)
+    const Layout L = layout(si, *sup);
+    hipError_t e = amtk::launch_sparse_attn_windowed(s, sup->key_block, sup->k, q, k, v, idx, count,
+                                                     o, nullptr,
+                                                     static_cast<unsigned char*>(ws) + L.cand,
+                                                     L.count - L.cand, st);
     return e == hipSuccess ? AMTK_OK : hip_fail(e);
   }
   // fused realisation: the indexer's LSE pass, then one kernel per block of

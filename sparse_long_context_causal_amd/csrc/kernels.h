@@ -68,6 +68,15 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
                               const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream);
+// The same in key windows (one launch per window, partial softmax merged
+// into o); scratch of sparse_windowed_scratch_bytes. Falls back to
+// launch_sparse_attn where the windowed form does not apply.
+size_t sparse_windowed_scratch_bytes(const LayerShape& s);
+hipError_t launch_sparse_attn_windowed(const LayerShape& s, int key_block, int max_units,
+                                       const void* q, const void* k, const void* v,
+                                       const int32_t* idx, const int32_t* count, float* o,
+                                       float* lse_sparse, void* scratch, size_t scratch_bytes,
+                                       hipStream_t stream);
 
 // Attention of each selection block's queries on the block's shared
 // support: the ids and count of the block's first row serve all of its rows,

@@ -456,7 +456,8 @@ template <bool kUnitTokens>   // true: key_block == 1; false: key_block % 16 == 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
-    float* __restrict__ lse_out, int n, int key_block, int max_units, float c) {
+    float* __restrict__ lse_out, int n, int key_block, int max_units, float c,
+    const int32_t* __restrict__ wstart, int nwin, int win) {
   constexpr int D = 128, HKV = 8, G = 4, HQ = HKV * G;
   constexpr unsigned kRowBytes = HKV * D * sizeof(bf16_t);   // one token, all KV heads
   __shared__ __align__(256) unsigned char smem[2 * kTileBytes];   // keys, values of a chunk
@@ -464,7 +465,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   const int i = n - 1 - (int)(blockIdx.x / HKV);   // longest rows first
   const int g = (int)(blockIdx.x % HKV);
   const int m = lane & 15, q = lane >> 4;
-  const int cnt = min(max(count[i], 0), max_units);
+  int cnt = min(max(count[i], 0), max_units);
+  // Key windows (nwin > 0): this launch takes the support's units that lie
+  // in window win, positions wstart[win] .. wstart[win + 1] of the row, and
+  // merges its partial softmax with the earlier windows' (O normalised,
+  // lse_out the running LSE). A row whose ids are not ascending
+  // (wstart[0] < 0) is done whole in window 0.
+  int s0 = 0;
+  if (nwin > 0) {
+    const int32_t* ws = wstart + (size_t)i * (nwin + 1);
+    if (ws[0] >= 0) {
+      s0 = ws[win];
+      cnt = ws[win + 1] - s0;
+    } else if (win > 0) {
+      cnt = 0;
+    }
+    if (win > 0 && cnt <= 0) return;   // nothing in this window: keep the earlier result
+  }
+  const bool merge = nwin > 0 && win > 0;
+  const int lim = max_units - 1 - s0;   // last readable position after the shift
   const int total = cnt * key_block;
   const int nch = (total + 31) >> 5;
   if (nch == 0) {   // empty support: zero output, LSE -inf
@@ -472,7 +491,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     if (lse_out && lane < G) lse_out[(size_t)(G * g + lane) * n + i] = -INFINITY;
     return;
   }
-  const int32_t* ids = idx + (size_t)i * max_units;
+  const int32_t* ids = idx + (size_t)i * max_units + s0;
   unsigned char* kbuf = smem;
   unsigned char* vbuf = smem + kTileBytes;
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K) + g * (D * 2);
@@ -489,11 +508,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     const int t0 = ch << 5;
     if constexpr (kUnitTokens) {
 #pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) raw[c8] = ids[min(t0 + 4 * c8 + q, max_units - 1)];
-      raw[8] = ids[min(t0 + (lane & 31), max_units - 1)];
+      for (int c8 = 0; c8 < 8; ++c8) raw[c8] = ids[min(t0 + 4 * c8 + q, lim)];
+      raw[8] = ids[min(t0 + (lane & 31), lim)];
     } else {
-      raw[0] = ids[min(t0 / key_block, max_units - 1)];
-      raw[4] = ids[min((t0 + 16) / key_block, max_units - 1)];
+      raw[0] = ids[min(t0 / key_block, lim)];
+      raw[4] = ids[min((t0 + 16) / key_block, lim)];
     }
   };
   // key/value row of token rr of the chunk starting at t0, given its raw id
@@ -647,18 +666,85 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   // write heads 0, 1 and lanes of group 1 heads 2, 3 (d = 16 blk + m).
   const bool upper = q == 1;
   float* orow = O + ((size_t)i * HQ + G * g + (upper ? 2 : 0)) * D + m;
+  // this window's LSE of head lane%4 (log2 units)
+  const float lw = l > 0.f ? mrun + log2f(l) : -INFINITY;
+  float lnew = lw;
+  if (merge) {
+    // O = O_old * exp(L_old - L) + O_win * exp(L_win - L), L = logaddexp
+    const float lold = lse_out[(size_t)(G * g + (lane & 3)) * n + i] * kLog2e;
+    const float mx = fmaxf(lold, lw);
+    float wa = 1.f, wb = 0.f;
+    lnew = lold;
+    if (lw > -INFINITY) {
+      const float ea = fast_exp2(lold - mx), eb = fast_exp2(lw - mx);
+      const float sum = ea + eb;
+      lnew = mx + log2f(sum);
+      wa = ea / sum;
+      wb = eb / sum;
+    }
+    const float wa0 = quad_bcast<0>(wa), wa1 = quad_bcast<1>(wa);
+    const float wa2 = quad_bcast<2>(wa), wa3 = quad_bcast<3>(wa);
+    const float wb0 = quad_bcast<0>(wb) * i0, wb1 = quad_bcast<1>(wb) * i1;
+    const float wb2 = quad_bcast<2>(wb) * i2, wb3 = quad_bcast<3>(wb) * i3;
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) {
-    f32x4 t = acc[bb];
+    for (int bb = 0; bb < 8; ++bb) {
+      f32x4 t = acc[bb];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], 16, 64);
-    if (q < 2) {
-      orow[16 * bb] = upper ? t[2] * i2 : t[0] * i0;
-      orow[D + 16 * bb] = upper ? t[3] * i3 : t[1] * i1;
+      for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], 16, 64);
+      if (q < 2) {
+        const float o0 = orow[16 * bb], o1 = orow[D + 16 * bb];
+        orow[16 * bb] = upper ? fmaf(o0, wa2, t[2] * wb2) : fmaf(o0, wa0, t[0] * wb0);
+        orow[D + 16 * bb] = upper ? fmaf(o1, wa3, t[3] * wb3) : fmaf(o1, wa1, t[1] * wb1);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      f32x4 t = acc[bb];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], 16, 64);
+      if (q < 2) {
+        orow[16 * bb] = upper ? t[2] * i2 : t[0] * i0;
+        orow[D + 16 * bb] = upper ? t[3] * i3 : t[1] * i1;
+      }
     }
   }
   if (lse_out && lane < 4)
-    lse_out[(size_t)(G * g + lane) * n + i] = l > 0.f ? (mrun + log2f(l)) * kLn2 : -INFINITY;
+    lse_out[(size_t)(G * g + lane) * n + i] = lnew > -INFINITY ? lnew * kLn2 : -INFINITY;
+}
+
+// Start of each key window in every row's support (see the windowed gather
+// below): out[i][w] = the first position of row i whose unit lies in window
+// w or later, out[i][nwin] = the row's count; out[i][0] = -1 marks a row
+// whose ids are not ascending. One wave per row.
+__global__ __launch_bounds__(256) void support_windows_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int n, int max_units,
+    int key_block, int win_tokens, int nwin, int32_t* __restrict__ out) {
+  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;   // (uniform per wave)
+  const int cnt = min(max(count[row], 0), max_units);
+  const int32_t* ids = idx + (size_t)row * max_units;
+  int32_t* o = out + (size_t)row * (nwin + 1);
+  auto win_of = [&](int u) -> int {
+    const long long t = (long long)max(u, 0) * key_block / win_tokens;
+    return (int)min(t, (long long)(nwin - 1));
+  };
+  bool bad = false;
+  for (int t = lane; t < cnt; t += 64) {
+    const int u = ids[t];
+    int wp = 0;
+    if (t > 0) {
+      const int up = ids[t - 1];
+      bad |= u < up;
+      wp = win_of(up);
+    }
+    for (int w = wp + 1; w <= win_of(u); ++w) o[w] = t;
+  }
+  const int wl = cnt > 0 ? win_of(ids[cnt - 1]) : 0;
+  for (int w = wl + 1 + lane; w <= nwin; w += 64) o[w] = cnt;
+  const bool any_bad = __ballot(bad) != 0ull;
+  if (lane == 0) o[0] = any_bad ? -1 : 0;
 }
 
 template <typename T, int E, int G>
@@ -726,7 +812,7 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
     hipLaunchKernelGGL(kern, dim3((unsigned)s.n * 8u), dim3(64), 0, stream,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                        static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, key_block,
-                       max_units, s.scale * kLog2e);
+                       max_units, s.scale * kLog2e, nullptr, 0, 0);
     return hipGetLastError();
   }
   if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32) {
@@ -741,6 +827,69 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
   if (s.dtype == kBF16)
     return attn_by_e<bf16_t>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
   return attn_by_e<float>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
+}
+
+// ------------------------------------------------------- windowed gather
+// The per-row kernel above draws its keys and values from all of the row's
+// history at once; at long N the rows in flight on one XCD touch far more
+// K/V than its L2 holds. The windowed form walks the supports in key
+// windows of kWindowTokens tokens (one KV head's keys and values of a
+// window fill one XCD's 4 MB L2), one launch per window, each launch taking
+// every row's units in that window and merging its partial softmax into
+// the output (normalised O plus the running LSE). Rows below the window's
+// first token have no keys there and are not launched.
+constexpr int kWindowTokens = 8192;
+constexpr int kMaxWindows = 64;
+
+static bool windowed_shape(const LayerShape& s, int key_block) {
+  return s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32 &&
+         (key_block == 1 || key_block % 16 == 0);
+}
+
+static int window_tokens(const LayerShape& s) {
+  const long long per = ((long long)s.n + kMaxWindows - 1) / kMaxWindows;
+  const long long w = (per + 63) / 64 * 64;
+  return (int)(w > kWindowTokens ? w : kWindowTokens);
+}
+
+static int window_count(const LayerShape& s) {
+  const int w = window_tokens(s);
+  return (int)(((long long)s.n + w - 1) / w);
+}
+
+size_t sparse_windowed_scratch_bytes(const LayerShape& s) {
+  const size_t starts = (size_t)s.n * (size_t)(window_count(s) + 1) * sizeof(int32_t);
+  const size_t lse = (size_t)s.hq * (size_t)s.n * sizeof(float);
+  return ((starts + 255) & ~(size_t)255) + ((lse + 255) & ~(size_t)255);
+}
+
+hipError_t launch_sparse_attn_windowed(const LayerShape& s, int key_block, int max_units,
+                                       const void* q, const void* k, const void* v,
+                                       const int32_t* idx, const int32_t* count, float* o,
+                                       float* lse_sparse, void* scratch, size_t scratch_bytes,
+                                       hipStream_t stream) {
+  const int nwin = window_count(s);
+  if (!windowed_shape(s, key_block) || nwin < 2 || !scratch ||
+      scratch_bytes < sparse_windowed_scratch_bytes(s))
+    return launch_sparse_attn(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
+  const int wt = window_tokens(s);
+  unsigned char* b = static_cast<unsigned char*>(scratch);
+  int32_t* starts = reinterpret_cast<int32_t*>(b);
+  const size_t sb = ((size_t)s.n * (size_t)(nwin + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  float* lse_run = lse_sparse ? lse_sparse : reinterpret_cast<float*>(b + sb);
+  hipLaunchKernelGGL(support_windows_kernel, dim3((unsigned)((s.n + 3) / 4)), dim3(256), 0, stream,
+                     idx, count, s.n, max_units, key_block, wt, nwin, starts);
+  hipError_t e = hipGetLastError();
+  auto kern = key_block == 1 ? sparse_attn_mfma_kernel<true> : sparse_attn_mfma_kernel<false>;
+  for (int w = 0; w < nwin && e == hipSuccess; ++w) {
+    const long long rows = (long long)s.n - (long long)w * wt;   // rows >= the window's first token
+    hipLaunchKernelGGL(kern, dim3((unsigned)rows * 8u), dim3(64), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), idx, count, o, lse_run, s.n, key_block,
+                       max_units, s.scale * kLog2e, starts, nwin, w);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace amtk

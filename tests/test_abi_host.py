@@ -135,6 +135,25 @@ def test_sparse_attn_validation(lib):
     assert f(ctypes.byref(a), 1, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
 
 
+def test_sparse_attn_windowed_validation(lib):
+    from sparse_long_context_causal_amd import _abi
+    f = lib.sparse_attn_windowed
+    b = _abi.AttnDesc(100000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_sparse_attn_workspace(ctypes.byref(b), ctypes.byref(need)) == 0
+    # window starts [n][windows + 1] int32 (13 windows of 8192 at 100000) + the running LSE
+    starts = (100000 * 14 * 4 + 255) // 256 * 256
+    assert need.value == starts + (32 * 100000 * 4 + 255) // 256 * 256
+    assert lib.amtk_sparse_attn_workspace(ctypes.byref(b), None) == -1
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert f(ctypes.byref(b), 1, 0, *args, FAKE, need.value, None) == -1        # max_units
+    assert f(ctypes.byref(b), 3, 4, *args, FAKE, need.value, None) == -2        # key_block
+    assert f(ctypes.byref(b), 1, 4, *args, None, need.value, None) == -1        # no scratch
+    assert f(ctypes.byref(b), 1, 4, *args, FAKE, need.value - 1, None) == -3    # too small
+    odd = ctypes.c_void_p(0x100080)   # scratch must be 256-byte aligned
+    assert f(ctypes.byref(b), 1, 4, *args, odd, need.value, None) == -1
+
+
 def test_sparse_attn_blocks_validation(lib):
     f = lib.sparse_attn_blocks
     a, _ = _descs()

@@ -1,0 +1,150 @@
+"""GPU parity of the windowed gather (sparse_attn_windowed): the supports
+walked in key windows of 8192 tokens, one launch per window, each window's
+partial softmax merged into the output by its LSE.
+
+Against the one-pass gather on the same supports (the merge only reorders
+fp32 sums: 1e-5 max abs on O and LSE) and against the oracle's attention on
+sampled rows (2e-3, the bf16 output bar). Supports span several windows and
+include rows whose ids are not ascending (attended whole in the first
+window), empty rows, invalid ids (negative, after the row, past the count)
+and rows inside the first window only.
+"""
+import numpy as np
+import pytest
+
+from oracle import OracleLayer, tokens_of_blocks
+from synth import random_inputs
+from tests.gpu_helpers import TOL_OUT, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL_MERGE = 1e-5
+
+
+def _token_supports(n, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.full((n, k), -1, dtype=np.int32)
+    cnt = np.zeros(n, dtype=np.int32)
+    for i in range(n):
+        m = min(k, i + 1)
+        if i + 1 > 4 * m:   # m of the distinct draws, spread over the whole row
+            pool = np.unique(rng.integers(0, i + 1, 2 * m))
+            ids = np.sort(rng.choice(pool, min(m, pool.size), replace=False))
+        else:
+            ids = np.sort(rng.choice(i + 1, m, replace=False))
+        idx[i, : ids.size] = ids
+        cnt[i] = ids.size
+    # not ascending: shuffled rows (one pass, in the first window)
+    for i in rng.choice(np.arange(k, n), 40, replace=False):
+        rng.shuffle(idx[i, : cnt[i]])
+    # invalid entries: a negative id and an id after the row, at the end of
+    # ascending rows (ascending order kept: -1 first, the late id last)
+    for i in rng.choice(np.arange(k, n), 20, replace=False):
+        idx[i, 0] = -1
+        idx[i, cnt[i] - 1] = min(n - 1, i + 5)
+    cnt[rng.choice(n, 10, replace=False)] = 0
+    # past the valid entries: -1 padding read (short rows), or clamped at k
+    cnt[rng.choice(k - 3, 5, replace=False)] += 3
+    cnt[rng.choice(np.arange(k, n), 5, replace=False)] += 3
+    cnt = np.minimum(cnt, k + 7).astype(np.int32)
+    return idx, cnt
+
+
+def _row_tokens(idx, cnt, i, k, key_block=1):
+    c = min(max(int(cnt[i]), 0), k)
+    units = [int(u) for u in idx[i, :c] if u >= 0]
+    if key_block == 1:
+        return sorted(j for j in units if j <= i)
+    return tokens_of_blocks(np.array([u for u in units if u * key_block <= i]), key_block, i)
+
+
+def _run_both(amtk, d, idx, cnt, key_block, want_lse):
+    import torch
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    o1, l1 = amtk.sparse_attn(d["q"], d["k"], d["v"], ti, tc, key_block, want_lse=True)
+    o2, l2 = amtk.sparse_attn_windowed(d["q"], d["k"], d["v"], ti, tc, key_block, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return o1.cpu().numpy(), l1.cpu().numpy(), o2.cpu().numpy(), (l2.cpu().numpy() if want_lse else None)
+
+
+def _compare(o1, l1, o2, l2):
+    assert np.all(np.isfinite(o2))
+    assert float(np.max(np.abs(o1 - o2))) <= TOL_MERGE
+    if l2 is not None:
+        fin = np.isfinite(l1)
+        assert np.array_equal(fin, np.isfinite(l2))
+        assert float(np.max(np.abs(l1[fin] - l2[fin]))) <= TOL_MERGE
+
+
+@pytest.mark.parametrize("want_lse", [True, False])
+def test_windowed_token_supports(gpu_lib, want_lse):
+    n, k = 20000, 300            # three windows: 8192, 8192, 3616 tokens
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=77, sink=True)
+    d = upload(x, "bf16")
+    idx, cnt = _token_supports(n, k, 78)
+    o1, l1, o2, l2 = _run_both(gpu_lib, d, idx, cnt, 1, want_lse)
+    _compare(o1, l1, o2, l2)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in (0, 8191, 8192, 12345, 16384, 19999):
+        toks = _row_tokens(idx, cnt, i, k)
+        if not toks:
+            assert np.all(o2[i] == 0)
+            continue
+        o_ref, l_ref = layer.attention_on(i, toks)
+        assert float(np.max(np.abs(o2[i].astype(np.float64) - o_ref))) <= TOL_OUT["bf16"], f"row {i}"
+        if l2 is not None:
+            assert float(np.max(np.abs(l2[:, i] - l_ref))) <= 1e-3, f"row {i} lse"
+
+
+def test_windowed_key_block_supports(gpu_lib):
+    n, k, kb = 17000, 12, 64     # 266 key blocks over three windows
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=81, sink=True)
+    d = upload(x, "bf16")
+    rng = np.random.default_rng(82)
+    idx = np.full((n, k), -1, dtype=np.int32)
+    cnt = np.zeros(n, dtype=np.int32)
+    for i in range(n):
+        nb = i // kb + 1
+        m = min(k, nb)
+        ids = np.sort(rng.choice(nb, m, replace=False))
+        idx[i, :m] = ids
+        cnt[i] = m
+    for i in rng.choice(np.arange(2000, n), 25, replace=False):
+        rng.shuffle(idx[i, : cnt[i]])
+    o1, l1, o2, l2 = _run_both(gpu_lib, d, idx, cnt, kb, True)
+    _compare(o1, l1, o2, l2)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in (5, 8200, 16999):
+        toks = _row_tokens(idx, cnt, i, k, kb)
+        o_ref, _ = layer.attention_on(i, toks)
+        assert float(np.max(np.abs(o2[i].astype(np.float64) - o_ref))) <= TOL_OUT["bf16"], f"row {i}"
+
+
+def test_windowed_one_window_is_sparse_attn(gpu_lib):
+    """n within one window: the call is the one-pass gather, bit for bit."""
+    n, k = 3000, 40
+    x = random_inputs(n, 32, 8, 128, "bf16", seed=85, sink=True)
+    d = upload(x, "bf16")
+    idx, cnt = _token_supports(n, k, 86)
+    o1, l1, o2, l2 = _run_both(gpu_lib, d, idx, cnt, 1, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_windowed_repeat_and_shrink(gpu_lib):
+    """Two calls in a row on one scratch, the second on a smaller layer: the
+    scratch keeps nothing that the next call reads unwritten."""
+    import torch
+    amtk = gpu_lib
+    ws = None
+    for n, seed in ((20000, 91), (9000, 93)):
+        x = random_inputs(n, 32, 8, 128, "bf16", seed=seed, sink=True)
+        d = upload(x, "bf16")
+        idx, cnt = _token_supports(n, 64, seed + 1)
+        ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+        if ws is None:
+            ws = amtk.workspace(amtk.sparse_attn_workspace_bytes(amtk.attn_desc(d["q"], d["k"])),
+                                d["q"].device)
+        o1, _ = amtk.sparse_attn(d["q"], d["k"], d["v"], ti, tc, 1)
+        o2, _ = amtk.sparse_attn_windowed(d["q"], d["k"], d["v"], ti, tc, 1, ws=ws)
+        torch.cuda.synchronize()
+        assert float((o1 - o2).abs().max()) <= TOL_MERGE
