@@ -64,7 +64,9 @@ def support_tokens(plan, key_block, query_block=1):
 
 
 def algorithmic_work(w, n, k, sup, gathered=None, units_read=None):
-    """Per-launch algorithmic flops / bytes of each kernel (see the design notes).
+    """Per-call algorithmic flops / bytes of each stage (one call of a stage is one
+    launch, except the windowed gather: its window-start kernel and one launch
+    per key window; see the design notes).
 
     sup: keys attended over all rows; gathered: key rows the sparse kernel
     must fetch (= sup per row; once per selection block when shared);
@@ -82,7 +84,8 @@ def algorithmic_work(w, n, k, sup, gathered=None, units_read=None):
 
 
 def traffic_for(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, if still current."""
+    """Bytes from beyond L2 per call of a stage (all its launches) from the committed
+    counter summary, if still current."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -90,7 +93,7 @@ def traffic_for(kernel, workload):
     ent = t.get(workload, {}).get(kernel)
     if not ent or ent.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
         return None
-    return ent.get("hbm_bytes_per_launch")
+    return ent.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(w, x, k, key_block, budget_s=25.0, query_block=1):

@@ -2,8 +2,8 @@
 walked in key windows of 8192 tokens, one launch per window, each window's
 partial softmax merged into the output by its LSE.
 
-Against the one-pass gather on the same supports (the merge only reorders
-fp32 sums: 1e-5 max abs on O and LSE) and against the oracle's attention on
+Against the one-pass gather on the same supports (1.5e-4 max abs on O and
+LSE: the windows round the bf16 weight split differently) and against the oracle's attention on
 sampled rows (2e-3, the bf16 output bar). Supports span several windows and
 include rows whose ids are not ascending (attended whole in the first
 window), empty rows, invalid ids (negative, after the row, past the count)
@@ -18,7 +18,12 @@ from tests.gpu_helpers import TOL_OUT, upload
 
 pytestmark = pytest.mark.gpu
 
-TOL_MERGE = 1e-5
+# Each window weighs its keys against its own maximum, so the bf16 hi/lo
+# split of the weights rounds differently from the one-pass gather's. Each
+# gather is within 2^-16 * max|V| of the exact output, so the two differ by
+# at most 2^-15 * max|V| (|V| <= ~5 for these inputs): 1.5e-4, well inside
+# the 2e-3 output bar.
+TOL_MERGE = 1.5e-4
 
 
 def _token_supports(n, k, seed):
