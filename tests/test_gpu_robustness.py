@@ -90,6 +90,37 @@ def test_sparse_attn_writes_every_element(gpu_lib, kb):
     assert _clean(o2) and not bool(torch.isnan(lse2.cpu()).any())
 
 
+@pytest.mark.parametrize("kb", [1, 64])
+def test_sparse_attn_windowed_writes_every_element(gpu_lib, kb):
+    """Two key windows (N = 9000): rows with empty supports, rows whose ids all
+    lie in the second window, rows in random order."""
+    import torch
+    amtk = gpu_lib
+    n, k = 9000, 8
+    _, q, kk, v = _layer(n, 41 + kb)
+    rng = np.random.default_rng(40 + kb)
+    idx = np.full((n, k), -1, dtype=np.int32)
+    cnt = rng.integers(0, k + 1, n).astype(np.int32)
+    for i in range(n):
+        top = i if kb == 1 else i // 64
+        lo = 8192 // kb if (i % 3 == 0 and top >= 8192 // kb) else 0   # second window only
+        idx[i, : cnt[i]] = np.sort(rng.integers(lo, top + 1, cnt[i]))
+        if i % 7 == 0:
+            rng.shuffle(idx[i, : cnt[i]])
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    ad = amtk.attn_desc(q, kk)
+    ws = amtk.workspace(amtk.sparse_attn_workspace_bytes(ad), q.device)
+    o, lse = _poisoned((n, 32, 128), torch.float32), _poisoned((32, n), torch.float32)
+    amtk._call("sparse_attn_windowed", ctypes.byref(ad), kb, k, amtk._ptr(q), amtk._ptr(kk),
+               amtk._ptr(v), amtk._ptr(ti), amtk._ptr(tc), amtk._ptr(o), amtk._ptr(lse),
+               amtk._ptr(ws), ws.numel(), amtk._stream(q.device))
+    torch.cuda.synchronize()
+    assert _clean(o) and not bool(torch.isnan(lse.cpu()).any())
+    o1, _ = amtk.sparse_attn(q, kk, v, ti, tc, kb)
+    torch.cuda.synchronize()
+    assert float((o1 - o).abs().max()) <= 1.5e-4
+
+
 @pytest.mark.parametrize("qb", [1, 64])
 def test_indexer_paths_write_every_element(gpu_lib, qb):
     import torch
