@@ -167,24 +167,25 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   // busy together (left alone, the compiler issues the MFMAs in bursts that
   // stall the wave). The order is held by empty volatile asm statements
   // (which keep their program order): each one makes the next MFMA's key
-  // operand and the current head's score vector depend on the previous
-  // group's sums.
+  // operand and the next group's inputs depend on the previous group's sums.
   // The sums are formed in the same order as in stats(), so results match.
   constexpr bool kInterleave = std::is_same<T, bf16_t>::value && (G % 2 == 0);
   constexpr int kEpg = 16 / NC;   // elements of the current head per MFMA
-  auto step = [&](f32x16& nxt, uint4 (&kk)[NC], const uint4 (&qq)[NC], f32x16& cur,
+  auto step = [&](f32x16& nxt, uint4 (&kk)[NC], const uint4 (&qq)[NC], const f32x16& cur,
                   int h) __attribute__((always_inline)) {
     const float mc = mrun[h] * c;
     float s0 = 0.f, s1 = 0.f;
     nxt = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      // the whole score vector is tied (no element copies to make)
-      u32x4 kv = __builtin_bit_cast(u32x4, kk[cc]);
-      asm volatile("" : "+v"(kv), "+v"(cur) : "v"(s0), "v"(s1));
       float x[kEpg];
 #pragma unroll
       for (int e = 0; e < kEpg; ++e) x[e] = cur[cc * kEpg + e];
+      u32x4 kv = __builtin_bit_cast(u32x4, kk[cc]);
+      if constexpr (kEpg == 2)
+        asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]) : "v"(s0), "v"(s1));
+      else
+        asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "v"(s0), "v"(s1));
       kk[cc] = __builtin_bit_cast(uint4, kv);
       ChunkMma<T>::mma(nxt, kk[cc], qq[cc]);
 #pragma unroll
