@@ -540,7 +540,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
       off[c8] = (unsigned)(ok ? r : i) * kRowBytes + ((c8 & 1) ? xo1 : xo0);
     }
     int r;
-    const bool okt = token_row(t0, lane & 31, kUnitTokens ? raw[8] : ((lane & 16) ? raw[4] : raw[0]), r);
+    int own = raw[8];
+    if constexpr (!kUnitTokens) {   // a select, not an indexed access (which would go to scratch)
+      const int lo = raw[0], hi = raw[4];
+      own = (lane & 16) ? hi : lo;
+    }
+    const bool okt = token_row(t0, lane & 31, own, r);
     return (unsigned)__ballot(okt);   // lanes 0..31: tokens 0..31
   };
   const uint32_t kb_lds = lds_addr(kbuf), vb_lds = lds_addr(vbuf);

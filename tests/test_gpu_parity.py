@@ -535,7 +535,12 @@ def test_workload_indexer_bf16_32k_sampled(gpu_lib):
     check_support_rows(idx, cnt, None, rows, w.k,
                        scores=lambda i: (lambda r: (r["score"], r["kth"]))(ix.row(int(i), w.k, 64)))
     d = upload(x, "bf16")
-    out, _ = amtk.sparse_attn(d["q"], d["k"], d["v"], torch.from_numpy(idx).cuda(),
-                              torch.from_numpy(cnt).cuda(), 64)
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    out, _ = amtk.sparse_attn(d["q"], d["k"], d["v"], ti, tc, 64)
     layer = OracleLayer(x["q"], x["k"], x["v"])
     check_outputs_on_gpu_support(out.cpu().numpy(), None, layer, rows, idx, cnt, 64, "bf16")
+    # the windowed gather (four 8192-token windows) on the same supports
+    out_w, _ = amtk.sparse_attn_windowed(d["q"], d["k"], d["v"], ti, tc, 64)
+    torch.cuda.synchronize()
+    assert float((out_w - out).abs().max()) <= 1.5e-4
+    check_outputs_on_gpu_support(out_w.cpu().numpy(), None, layer, rows, idx, cnt, 64, "bf16")
