@@ -6,8 +6,10 @@
 // (token ids, or 64-token key blocks from the indexer); the softmax is taken
 // over the support only. The abstract states the same recompute step.
 //
-// Three kernels. bf16 with d = 128 and 8 KV heads x 4 query heads runs on
-// MFMAs (sparse_attn_mfma_kernel, at the end of this file). The other
+// Three attention kernels. bf16 with d = 128 and 8 KV heads x 4 query heads
+// runs on MFMAs (sparse_attn_mfma_kernel, near the end of this file), in one
+// pass or in key windows (support_windows_kernel finds where each window
+// starts in every row's support; the windowed gather closes the file). The other
 // shapes use one wavefront per query row, rows issued longest first: all Hq
 // heads share the row's support, so one gathered token row K[j] (all Hkv
 // heads, d contiguous: Hkv*d elements) serves every head. In the generic
