@@ -323,27 +323,29 @@ __device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* words,
   rs.btau[r] = bt;
 }
 
-// The same for a row whose state the caller already holds (cnt = candidates
-// appended so far; seen, cge and bt as stored): the histogram words of the
-// next 8 bins come in one batch of reads, as the bound rarely moves further.
-__device__ __forceinline__ void raise_bound_from(RowState& rs, const unsigned* words, int r,
-                                                 int budget, int cnt, int seen, int cge, int bt) {
+// The same on row state held in registers (cnt = candidates appended so
+// far; seen, cge and bt as last left): every lane serving the row runs it,
+// so all of them keep the same state. The histogram words of the next 8
+// bins come in one batch of reads, as the bound rarely moves further.
+__device__ __forceinline__ void raise_bound_regs(const unsigned* words, int budget, int cnt,
+                                                 int& seen, int& cge, int& bt) {
   int cg = cge + (cnt - seen);
   const int w0 = bt >> 1;
   unsigned wv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) wv[j] = words[min(w0 + j, kFBinWords - 1)];
-  while (bt < kFBins - 1) {
-    const int j = (bt >> 1) - w0;
-    const unsigned w = j == 0 ? wv[0] : j == 1 ? wv[1] : j == 2 ? wv[2] : j == 3 ? wv[3] : words[bt >> 1];
-    const int hb = (int)((w >> ((bt & 1) * 16)) & 0xffffu);
+  int b = bt;
+  while (b < kFBins - 1) {
+    const int j = (b >> 1) - w0;
+    const unsigned w = j == 0 ? wv[0] : j == 1 ? wv[1] : j == 2 ? wv[2] : j == 3 ? wv[3] : words[b >> 1];
+    const int hb = (int)((w >> ((b & 1) * 16)) & 0xffffu);
     if (cg - hb < budget) break;
     cg -= hb;
-    ++bt;
+    ++b;
   }
-  rs.seen[r] = cnt;
-  rs.cge[r] = cg;
-  rs.btau[r] = bt;
+  seen = cnt;
+  cge = cg;
+  bt = b;
 }
 
 // Swizzled partial-mass layout: element (register r, source lane) of KV head
@@ -484,6 +486,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     }
   };
   float blk = 0.f;   // KB > 1: this query's mass over the current key block (this wave's heads)
+  // KB = 1: the filter state of the row this lane serves, kept in registers
+  // (the same in every lane of the row's group; written to rs at the end)
+  int r_cnt = 0, r_seen = 0, r_cge = 0, r_bt = 0;
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
@@ -547,10 +552,8 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       // A mass passes the bound bin exactly when its bit pattern is at least
       // the bin's floor pattern, so the bin itself is only formed for the
       // histogram of appended entries.
-      const int bt = rs.btau[own_n];
-      const int pos0 = rs.cnt[own_n];
-      const int seen = rs.seen[own_n], cge = rs.cge[own_n];
-      const unsigned thr = filter_bin_floor_bits(bt);
+      const int pos0 = r_cnt;
+      const unsigned thr = filter_bin_floor_bits(r_bt);
       int pos = pos0;
       const bool live = own_ok && pos <= cap;
       // Lane j of a row's lane group takes the row's keys k0 + m with
@@ -599,9 +602,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       }
       // the bound can only rise after appends (the histogram is unchanged
       // otherwise)
-      if (own_j == 0 && own_ok && pos != pos0) {
-        rs.cnt[own_n] = pos;
-        if (pos <= cap) raise_bound_from(rs, own_hist, own_n, budget, pos, seen, cge, bt);
+      if (pos != pos0) {   // (uniform over the row's group; never for rows past n)
+        r_cnt = pos;
+        if (pos <= cap) raise_bound_regs(own_hist, budget, pos, r_seen, r_cge, r_bt);
       }
     } else {
       // ---- key blocks of KB = 64 tokens = two key tiles
@@ -636,6 +639,12 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   }
   wait_vmem_all();
   if constexpr (CS) return;
+  if constexpr (KB == 1) {
+    if (own_j == 0) {
+      rs.cnt[own_n] = r_cnt;
+      rs.btau[own_n] = r_bt;
+    }
+  }
   __syncthreads();
   if (threadIdx.x < 32) {
     const int qq = q0 + threadIdx.x;
