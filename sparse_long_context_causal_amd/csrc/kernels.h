@@ -32,6 +32,7 @@ struct CandidatePool {
 };
 
 constexpr int kMaxBudget = 8192;      // largest k the select kernel sorts in LDS
+constexpr size_t kLdsBytesPerCu = 160 * 1024;   // LDS of one gfx950 CU (one workgroup's maximum)
 constexpr int kMaxQRow = 8192;        // largest Hq*d held in LDS by the overflow path
 constexpr int kFallbackSlots = 128;   // concurrent overflow rows
 

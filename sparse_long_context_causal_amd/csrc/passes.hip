@@ -348,13 +348,18 @@ __device__ __forceinline__ void raise_bound_regs(const unsigned* words, int budg
   bt = b;
 }
 
-// Swizzled partial-mass layout: element (register r, source lane) of KV head
-// g's tile lives at word r*64 + (lane ^ 4r) of that head's 4 KiB block, so
-// both the lane-major writes and the row-owner reads are bank-conflict free.
-// The whole index is (g*1024 + lane) ^ (68*r): one base per lane and an XOR
-// with a constant per register.
+// Partial-mass layout: element (register r, source lane) of KV head g's
+// tile lives at word g*kPartHead + r*kPartPitch + lane. The pitch of 68
+// words puts register r of lane l in bank (4r + l) mod 64, so the
+// lane-major writes and the row-owner reads (one source lane, registers
+// 0..7 across a row's lanes, four adjacent source lanes per wave) are
+// bank-conflict free, and each write is one base plus a constant offset.
+// A head's block of 17 x 64 words keeps the heads 64-word aligned for
+// paired reads.
+constexpr int kPartPitch = 68;
+constexpr int kPartHead = 17 * 64;
 __device__ __forceinline__ int part_index(int g, int r, int src_lane) {
-  return (g * 16 + r) * 64 + (src_lane ^ (4 * r));
+  return g * kPartHead + r * kPartPitch + src_lane;
 }
 
 // HK: the KV heads if fixed at 8, else 0. CS: instead of filtering each
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   unsigned* hist = reinterpret_cast<unsigned*>(smem);                       // [32][kFBinWords]
   RowState& rs = *reinterpret_cast<RowState*>(hist + 32 * kFBinWords);
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(&rs) + sizeof(RowState));
-  const int part_floats = (KB == 1) ? hkv * 16 * 64 : hkv * 32;           // one buffer
+  const int part_floats = (KB == 1) ? hkv * kPartHead : hkv * 32;        // one buffer
   // key slots start on a 1 KiB boundary (the key-tile swizzle needs slots
   // aligned to the row pitch)
   unsigned char* slots = smem + ((reinterpret_cast<unsigned char*>(part + 2 * part_floats) - smem + 1023) & ~(ptrdiff_t)1023);
@@ -544,9 +549,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     }
     if constexpr (KB == 1) {
       float* pb = part + (kt & 1) * part_floats;
-      const int wb = (kt & 1) * part_floats + g * 1024 + lane;   // = part_index(g, 0, lane) in this buffer
+      const int wb = (kt & 1) * part_floats + part_index(g, 0, lane);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part[wb ^ (68 * r)] = pacc[r];
+      for (int r = 0; r < 16; ++r) part[wb + kPartPitch * r] = pacc[r];
       barrier_lds();   // partial masses visible
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       // A mass passes the bound bin exactly when its bit pattern is at least
@@ -569,9 +574,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         float p = src[0];
         if constexpr (HK == 8) {
 #pragma unroll
-          for (int gg = 1; gg < 8; ++gg) p += src[gg * 16 * 64];
+          for (int gg = 1; gg < 8; ++gg) p += src[gg * kPartHead];
         } else {
-          for (int gg = 1; gg < hkv; ++gg) p += src[gg * 16 * 64];
+          for (int gg = 1; gg < hkv; ++gg) p += src[gg * kPartHead];
         }
         return p * inv_hq;
       };
@@ -677,7 +682,7 @@ static hipError_t run_pass1(const LayerShape& s, const void* q, const void* k, f
 template <typename T, int D>
 static size_t pass2_lds_bytes(int hkv, int key_block) {
   size_t b = 32 * kFBinWords * sizeof(unsigned) + sizeof(RowState);
-  b += 2 * ((key_block == 1) ? (size_t)hkv * 16 * 64 : (size_t)hkv * 32) * sizeof(float);
+  b += 2 * ((key_block == 1) ? (size_t)hkv * kPartHead : (size_t)hkv * 32) * sizeof(float);
   b = (b + 1023) & ~(size_t)1023;   // key slots on a 1 KiB boundary
   b += (size_t)hkv * KTile<T, D>::kBytes;
   return b;
@@ -726,7 +731,17 @@ bool pass_shape_supported(const LayerShape& s) {
   // the wave's G query tiles live in VGPRs: G*d*elem_bytes <= 1024 per row
   if (G * s.d * (s.dtype == kBF16 ? 2 : 4) > 1024) return false;
   if (s.hq * s.d > kMaxQRow) return false;
-  return s.dtype == kBF16 || s.dtype == kF32;
+  if (s.dtype != kBF16 && s.dtype != kF32) return false;
+  // both passes' LDS (pass 1: two key slots per wave; pass 2: one slot per
+  // wave, the histograms and the partial masses) within one CU's 160 KiB
+  const size_t slot = (size_t)s.d * (s.dtype == kBF16 ? 2 : 4) * 32;   // KTile<T, D>::kBytes
+  const size_t lds1 = 2 * (size_t)s.hkv * slot;
+  const size_t lds2 = s.dtype == kBF16
+                          ? (s.d == 64 ? pass2_lds_bytes<bf16_t, 64>(s.hkv, 1)
+                                       : pass2_lds_bytes<bf16_t, 128>(s.hkv, 1))
+                          : (s.d == 64 ? pass2_lds_bytes<float, 64>(s.hkv, 1)
+                                       : pass2_lds_bytes<float, 128>(s.hkv, 1));
+  return lds1 <= kLdsBytesPerCu && lds2 <= kLdsBytesPerCu;
 }
 
 #define AMTK_PASS_DISPATCH(FN, ...)                                                  \

@@ -75,6 +75,7 @@ def _topk(lib, a, s, ws_bytes=1, q=FAKE, ws=FAKE, idx=FAKE):
     (dict(hq=32, hkv=2), -2),          # 16 query heads per KV head
     (dict(hkv=16, hq=16), -2),         # more KV heads than pass waves
     (dict(dtype=1, d=128, hq=8, hkv=2), -2),   # fp32 group tile too large for registers
+    (dict(dtype=1, d=128, hq=16, hkv=8), -2),  # fp32 key slots of 8 waves exceed the LDS
 ])
 def test_invalid_arguments_are_rejected(lib, kw, code):
     a, s = _descs(**kw)
