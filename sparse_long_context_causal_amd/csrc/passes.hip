@@ -362,6 +362,28 @@ __device__ __forceinline__ int part_index(int g, int r, int src_lane) {
   return g * kPartHead + r * kPartPitch + src_lane;
 }
 
+// The 8 KV heads' partial masses of a lane's two keys (LDS byte addresses a0,
+// a1 of head 0), issued together with one wait: the owners of a tile run in
+// step after the barrier, so nothing else hides a second round trip.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+__device__ __forceinline__ void read_partials_hk8(uint32_t a0, uint32_t a1, f32x2 (&v)[8]) {
+  static_assert(kPartHead == 17 * 64, "head stride in 64-word units below");
+  asm volatile(
+      "ds_read2st64_b32 %0, %8 offset1:17\n\t"
+      "ds_read2st64_b32 %1, %8 offset0:34 offset1:51\n\t"
+      "ds_read2st64_b32 %2, %8 offset0:68 offset1:85\n\t"
+      "ds_read2st64_b32 %3, %8 offset0:102 offset1:119\n\t"
+      "ds_read2st64_b32 %4, %9 offset1:17\n\t"
+      "ds_read2st64_b32 %5, %9 offset0:34 offset1:51\n\t"
+      "ds_read2st64_b32 %6, %9 offset0:68 offset1:85\n\t"
+      "ds_read2st64_b32 %7, %9 offset0:102 offset1:119\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
 // HK: the KV heads if fixed at 8, else 0. CS: instead of filtering each
 // row, write the column sums of the mass over the tile's rows (selection
 // blocks of consecutive queries share one support; KB = 1 only).
@@ -583,8 +605,26 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       // with the KV heads fixed at 8 both masses are read in one batch first
       float pm[2];
       if constexpr (HK == 8) {
-        pm[0] = mass(0);
-        pm[1] = mass(1);
+        uint32_t ad[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int mo = e * lpq + own_j;
+          const int r = ((mo >> 3) << 2) | (mo & 3), h2 = (mo >> 2) & 1;
+          ad[e] = lds_addr(pb + part_index(0, r, own_n + 32 * h2));
+        }
+        f32x2 v[8];
+        read_partials_hk8(ad[0], ad[1], v);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {   // heads in order 0..7, as mass() sums them
+          float p = v[4 * e].x;
+          p += v[4 * e].y;
+#pragma unroll
+          for (int j = 1; j < 4; ++j) {
+            p += v[4 * e + j].x;
+            p += v[4 * e + j].y;
+          }
+          pm[e] = p * inv_hq;
+        }
       }
       for (int e = 0; e < epl; ++e) {
         const int mo = e * lpq + own_j;
