@@ -21,7 +21,7 @@
 
 namespace amtk {
 
-constexpr int kBsThreads = 256;
+constexpr int kBsThreads = 1024;   // 16 waves: the radix passes over up to N scores are the cost
 
 __global__ __launch_bounds__(kBsThreads) void block_topk_kernel(
     const float* __restrict__ colsum, int n, int bsel, int k, int32_t* __restrict__ idx,
