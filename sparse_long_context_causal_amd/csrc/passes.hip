@@ -290,6 +290,89 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   }
 }
 
+// ------------------------------------------- pass 1, one head split by keys
+// A single head (the head-collapsed indexer: Hq = Hkv = 1, d = 64) gives the
+// kernel above one wave per 32-row tile: too few waves to fill a CU. Here
+// kLseSplit waves share a tile, wave w taking key tiles w, w + kLseSplit, ...
+// with its own running maximum (two LDS slots each, two tiles ahead); the
+// waves' (max, sum) pairs meet in LDS at the end.
+constexpr int kLseSplit = 4;
+
+__global__ __launch_bounds__(64 * kLseSplit) void pass1_lse_split_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, float* __restrict__ lse, int n,
+    float c, float tau, int* __restrict__ zero_counter) {
+  typedef KTile<bf16_t, 64> KT;
+  constexpr int NC = KT::kChunks;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hf = lane >> 5, col = lane & 31;
+  const int ntiles = (n + 31) >> 5;
+  const int qt = ntiles - 1 - (int)blockIdx.x;
+  const int q0 = qt << 5;
+  unsigned char* slot0 = smem + (2 * wave) * KT::kBytes;
+  unsigned char* slot1 = slot0 + KT::kBytes;
+  float* red = reinterpret_cast<float*>(smem + 2 * kLseSplit * KT::kBytes);   // [wave][m, l][32]
+  if (blockIdx.x == 0 && threadIdx.x == 0 && zero_counter) *zero_counter = 0;
+
+  uint4 qc[1][NC];
+  load_q_tiles<bf16_t, 64, 1>(Q, min(q0 + col, n - 1), 1, 0, lane, qc);
+  wait_vmem_all();   // Q in registers before the DMA stream starts
+  KLane<bf16_t, 64> kl;
+  kl.init(lane, 1);
+  if (wave <= qt) kl.issue(K, n, 1, 0, wave << 5, slot0);
+  if (wave + kLseSplit <= qt) kl.issue(K, n, 1, 0, (wave + kLseSplit) << 5, slot1);
+  float m = kNegBig, l = 0.f;   // this lane's keys only (its half of each tile)
+  int i = 0;
+  for (int kt = wave; kt <= qt; kt += kLseSplit, ++i) {
+    unsigned char* slot = (i & 1) ? slot1 : slot0;
+    if (kt + kLseSplit <= qt) wait_vmem_below<NC>();   // the next tile's NC loads may fly on
+    else wait_vmem_all();
+    uint4 kc[NC];
+    kl.read(slot, kc);
+    if (kt + 2 * kLseSplit <= qt) kl.issue(K, n, 1, 0, (kt + 2 * kLseSplit) << 5, slot);
+    f32x16 a;
+    score_tile<bf16_t, NC>(a, kc, qc[0]);
+    if (kt == qt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (acc_row(r, hf) > col) a[r] = -INFINITY;
+    }
+    float tmax = a[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, a[r]);
+    const float mnew = fmaxf(m, tmax);
+    const float mc = mnew * c;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      s0 += fast_exp2(fmaf(a[r], c, -mc));
+      s1 += fast_exp2(fmaf(a[r + 1], c, -mc));
+    }
+    l = fmaf(l, fast_exp2((m - mnew) * c), s0 + s1);
+    m = mnew;
+  }
+  wait_vmem_all();
+  // the two halves of the wave, then the waves
+  const float mo = xor32f(m), lo = xor32f(l);
+  const float mh = fmaxf(m, mo);
+  const float lh = l * fast_exp2((m - mh) * c) + lo * fast_exp2((mo - mh) * c);
+  if (hf == 0) {
+    red[(2 * wave) * 32 + col] = mh;
+    red[(2 * wave + 1) * 32 + col] = lh;
+  }
+  __syncthreads();
+  if (wave == 0 && hf == 0 && q0 + col < n) {
+    float mm = red[col];
+#pragma unroll
+    for (int w = 1; w < kLseSplit; ++w) mm = fmaxf(mm, red[(2 * w) * 32 + col]);
+    float ll = 0.f;
+#pragma unroll
+    for (int w = 0; w < kLseSplit; ++w)
+      ll += red[(2 * w + 1) * 32 + col] * fast_exp2((red[(2 * w) * 32 + col] - mm) * c);
+    lse[q0 + col] = mm * tau + logf(ll);
+  }
+}
+
 // ------------------------------------------------------------------ pass 2
 struct RowState {
   int cnt[32];    // candidates appended (keeps counting past the capacity)
@@ -813,6 +896,14 @@ bool pass_shape_supported(const LayerShape& s) {
 
 hipError_t launch_pass1_lse(const LayerShape& s, const void* q, const void* k, float* lse,
                             int* zero_counter, hipStream_t stream) {
+  if (s.hq == 1 && s.hkv == 1 && s.d == 64 && s.dtype == kBF16) {   // one head: split by keys
+    const int ntiles = (s.n + 31) / 32;
+    const size_t lds = (size_t)2 * kLseSplit * KTile<bf16_t, 64>::kBytes + 2 * kLseSplit * 32 * sizeof(float);
+    hipLaunchKernelGGL(pass1_lse_split_kernel, dim3(ntiles), dim3(64 * kLseSplit), lds, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), lse, s.n,
+                       s.scale * kLog2e, s.scale, zero_counter);
+    return hipGetLastError();
+  }
   AMTK_PASS_DISPATCH(run_pass1, s, q, k, lse, zero_counter, stream);
 }
 
