@@ -491,7 +491,10 @@ def _indexer_run(amtk, qi, ki, k, key_block):
     return idx.cpu().numpy(), cnt.cpu().numpy(), mass.cpu().numpy()
 
 
-@pytest.mark.parametrize("n,k,kb", [(1000, 4, 64), (300, 16, 1), (64, 2, 64), (65, 1, 64)])
+# n = 1, 31 and 97 put fewer key tiles than waves in the split LSE pass (one
+# head: four waves per 32-row tile) and leave ragged last tiles
+@pytest.mark.parametrize("n,k,kb", [(1000, 4, 64), (300, 16, 1), (64, 2, 64), (65, 1, 64),
+                                    (1, 3, 1), (31, 5, 1), (97, 7, 1), (97, 1, 64)])
 def test_indexer_small(gpu_lib, n, k, kb):
     rng = np.random.default_rng(n + k)
     from synth import round_bf16
