@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64) void select_wave_kernel(
     const int* __restrict__ row_bin, int n, int cap, int key_block, int budget,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ mass) {
   constexpr int kCap = 64 * R;   // kept entries the LDS holds
-  constexpr int U = 8;           // pool loads in flight per lane
+  constexpr int U = 32;          // pool loads in flight per lane (the loop is latency bound)
   __shared__ unsigned sv[kCap];
   __shared__ unsigned si[kCap];
   const int lane = threadIdx.x;
