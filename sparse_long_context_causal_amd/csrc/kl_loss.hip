@@ -385,7 +385,24 @@ __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(const float* __restri
   const int ntiles = (n + 31) >> 5;
   const int e = (int)threadIdx.x * 8;   // 8 of the tile's 32 x 64 values
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  for (int qt = kt; qt < ntiles; ++qt) {
+  // four query tiles' partials in flight per step, summed in query-tile order
+  int qt = kt;
+  for (; qt + 4 <= ntiles; qt += 4) {
+    float4 x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t t = (size_t)(qt + u);
+      const float4* src = reinterpret_cast<const float4*>(dk_part + (t * (t + 1) / 2 + kt) * (32 * kKlDi) + e);
+      x[u] = src[0];
+      y[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a.x += x[u].x; a.y += x[u].y; a.z += x[u].z; a.w += x[u].w;
+      b.x += y[u].x; b.y += y[u].y; b.z += y[u].z; b.w += y[u].w;
+    }
+  }
+  for (; qt < ntiles; ++qt) {
     const float4* src = reinterpret_cast<const float4*>(dk_part + ((size_t)qt * (qt + 1) / 2 + kt) * (32 * kKlDi) + e);
     const float4 x = src[0], y = src[1];
     a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
