@@ -70,6 +70,58 @@ def test_worked_row3_outputs_and_blocks():
     assert rb["support"].tolist() == [2, 3]
 
 
+def _num_or_inf(expr):
+    return -math.inf if str(expr) == "-inf" else _num(expr)
+
+
+def test_worked_rows_kth_mass():
+    """The selection boundary (k-th largest mass) of every worked row and budget,
+    read off the hand-sorted masses; -inf where the row keeps all its units."""
+    g, layer = _worked_layer()
+    for i_s, exp in g["rows"].items():
+        i = int(i_s)
+        for kk, want in exp["kth"].items():
+            r = layer.row(i, int(kk))
+            want = _num_or_inf(want)
+            if want == -math.inf:
+                assert r["kth"] == -math.inf, (i, kk)
+            else:
+                assert r["kth"] == pytest.approx(want, abs=1e-12), (i, kk)
+            assert oracle.kth_score(r["p"], int(kk)) == r["kth"]
+    exp3 = g["rows"]["3"]
+    for kk, want in exp3["block2_kth"].items():
+        rb = layer.row(3, int(kk), key_block=2)
+        want = _num_or_inf(want)
+        if want == -math.inf:
+            assert rb["kth"] == -math.inf
+        else:
+            assert rb["kth"] == pytest.approx(want, abs=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_kth_score_is_the_order_statistic(seed):
+    """kth_score(x, k) is the value m with #(x > m) < k <= #(x >= m), the
+    definition of the k-th largest element, on rows with repeated values."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 40))
+    x = rng.integers(0, 6, size=n).astype(np.float64) / 7.0
+    for kk in range(1, n + 3):
+        m = oracle.kth_score(x, kk)
+        if n <= kk:
+            assert m == -math.inf
+            continue
+        assert m in set(x.tolist())
+        assert int(np.sum(x > m)) < kk <= int(np.sum(x >= m))
+        # the top-k set is exactly what lies above m plus the first equals
+        top = oracle.top_units(x, kk)
+        assert top.size == kk
+        assert np.all(x[top] >= m)
+        above = np.nonzero(x > m)[0]
+        assert set(above.tolist()) <= set(top.tolist())
+        eq_taken = sorted(set(top.tolist()) - set(above.tolist()))
+        assert eq_taken == np.nonzero(x == m)[0][: kk - above.size].tolist()
+
+
 # ---------------------------------------------------------- pages' sparsity
 def test_sparsity_matches_pages_sweep_ends():
     g = json.load(open(os.path.join(GOLDEN, "sparsity_sweep.json")))
