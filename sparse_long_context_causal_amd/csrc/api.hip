@@ -458,8 +458,10 @@ int indexer_prefill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale,
   if ((rc = indexer_shape(s.n, d_idx, s.dtype, idx_scale, &si))) return rc;
   if ((rc = check_support(sup))) return rc;
   if (!amtk::sparse_shape_supported(s)) return AMTK_E_UNSUPPORTED;
-  if (!v || !o || !idx || !count) return AMTK_E_INVALID;
-  if (!aligned(v, 16) || !aligned(o, 16)) return AMTK_E_INVALID;
+  // both realisations read the backbone q, k, v and write o, idx, count
+  if (!q || !k || !v || !o || !idx || !count) return AMTK_E_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return AMTK_E_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (sup->query_block == 1) {   // per-query realisation: indexer_topk, then sparse_attn
     rc = run_topk(si, *sup, 0, q_idx, k_idx, idx, count, mass, nullptr, ws, ws_bytes, st);
@@ -478,9 +480,8 @@ int indexer_prefill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale,
   if (sup->key_block == 1 || !amtk::shared_attn_shape_supported(s, sup->query_block) ||
       !amtk::indexer_shared_supported(si.n, si.d, si.dtype, sup->key_block, sup->query_block, sup->k))
     return AMTK_E_UNSUPPORTED;
-  if (!q_idx || !k_idx || !q || !k || !ws) return AMTK_E_INVALID;
-  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(q, 16) || !aligned(k, 16) ||
-      !aligned(idx, 4) || !aligned(count, 4) || !aligned(ws, 256) || (mass && !aligned(mass, 4)))
+  if (!q_idx || !k_idx || !ws) return AMTK_E_INVALID;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(ws, 256) || (mass && !aligned(mass, 4)))
     return AMTK_E_INVALID;
   const Layout L = layout(si, *sup);
   if (ws_bytes < L.total) return AMTK_E_WORKSPACE;

@@ -191,6 +191,14 @@ def test_indexer_prefill_validation(lib):
     assert ok(s_fused, a=a) == -2                       # not the tile kernel's layer shape
     assert ok(s_fused, outs=[None, FAKE, FAKE, None]) == -1
     assert ok(s_fused, args=[FAKE, FAKE, FAKE, None, FAKE]) == -1
+    # the per-query realisation checks the backbone q and k before any launch
+    odd = ctypes.c_void_p(0x100002)
+    s_query = _abi.SupportDesc(16, 1, 1, 0)
+    for bad in ([None, FAKE, FAKE, FAKE, FAKE], [FAKE, None, FAKE, FAKE, FAKE],
+                [odd, FAKE, FAKE, FAKE, FAKE], [FAKE, odd, FAKE, FAKE, FAKE]):
+        assert ok(s_query, args=bad) == -1
+        assert ok(_abi.SupportDesc(16, 64, 1, 0), args=bad) == -1
+        assert ok(s_fused, args=bad) == -1
 
 
 def test_diagnostics_validation(lib):
