@@ -72,6 +72,11 @@ typedef struct {
  * shapes (written to *bytes). Returns AMTK_OK or a validation error. */
 int amtk_topk_workspace(const amtk_attn_desc* attn, const amtk_support_desc* sup, size_t* bytes);
 
+/* The same figure as a plain return value: the workspace bytes of
+ * topk_support / oracle_prefill for these shapes, or 0 when the descriptors
+ * are invalid or unsupported (amtk_topk_workspace reports which). */
+size_t amtk_workspace_bytes(const amtk_attn_desc* attn, const amtk_support_desc* sup);
+
 /*
  * topk_support - the attention-mass top-k oracle's support selection.
  * [TB 2.1], [Abstract]: for every query row i the per-head causal softmax

@@ -36,6 +36,7 @@ _I64 = ctypes.c_int64
 
 SIGNATURES = {
     "amtk_topk_workspace": (ctypes.c_int, [_A, _S, ctypes.POINTER(_SZ)]),
+    "amtk_workspace_bytes": (_SZ, [_A, _S]),
     "topk_support": (ctypes.c_int, [_A, _S, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "topk_support_stage": (ctypes.c_int, [_A, _S, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparse_attn": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),

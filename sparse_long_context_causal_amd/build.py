@@ -3,6 +3,9 @@
 Every .hip file under csrc/ is compiled by hipcc to an object, in parallel,
 then linked into ``libamtk.so`` next to this file. Only the C-ABI symbols of
 include/amtk.h are exported (-fvisibility=hidden elsewhere).
+
+calib/*.hip (measurement kernels that are not part of the library: the L2
+read ceiling the gather is reported against) link into ``libamtk_calib.so``.
 """
 import concurrent.futures
 import os
@@ -14,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libamtk.so")
+CALIB_SRC = os.path.join(PKG, "calib")
+CALIB_LIB = os.path.join(PKG, "libamtk_calib.so")
 ARCH = os.environ.get("AMTK_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [
@@ -32,7 +37,8 @@ def _hipcc():
 
 
 def _compile(src):
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    sub = "calib_" if os.path.dirname(src) == CALIB_SRC else ""
+    obj = os.path.join(OBJ, sub + os.path.basename(src) + ".o")
     cmd = [_hipcc(), *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -40,21 +46,29 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
-    """Compile every csrc/*.hip and link libamtk.so. Always rebuilds."""
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=True):
+    """Compile every csrc/*.hip and link libamtk.so, and calib/*.hip into
+    libamtk_calib.so. Always rebuilds."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    calib = sorted(os.path.join(CALIB_SRC, f) for f in os.listdir(CALIB_SRC)
+                   if f.endswith(".hip"))
+    jobs = min(len(srcs) + len(calib), int(os.environ.get("MAX_JOBS", "8")))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs + calib))
+    _link(objs[: len(srcs)], LIB)
+    _link(objs[len(srcs):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -1,0 +1,114 @@
+// Read-bandwidth calibration of the on-chip L2 caches (gfx950), built as
+// libamtk_calib.so beside the library. It measures a ceiling for kernels whose
+// reads are served from L2 rather than HBM (the windowed gather): every XCD
+// re-reads a region of its own that fits its L2, so after the first pass all
+// reads hit that XCD's L2.
+//
+// Workgroups are handed to the 8 XCDs round robin, so workgroup b runs on
+// XCD b % 8 and reads region b % 8 of the buffer; the workgroups of one XCD
+// split its region among themselves.
+//   mode 0: contiguous 16-byte loads, 256 threads walking the region in
+//           strides (the plain streaming ceiling);
+//   mode 1: 256-byte rows at pseudo-random row positions of the region, one
+//           row per 16 lanes (the access shape of a row gather).
+// Nothing is written unless the XOR of everything read hits a fixed 128-bit
+// value, which keeps the loads alive without adding write traffic.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void l2_stream_kernel(const uint4* __restrict__ buf,
+                                                             long region, int iters,
+                                                             uint4* __restrict__ sink) {
+  const int xcd = blockIdx.x % kXcds;
+  const long local = blockIdx.x / kXcds;
+  const long per_xcd = gridDim.x / kXcds;
+  const uint4* base = buf + (long)xcd * region;
+  const long stride = per_xcd * kThreads;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (int it = 0; it < iters; ++it) {
+    long e = local * kThreads + threadIdx.x;
+    for (; e + (kUnroll - 1) * stride < region; e += kUnroll * stride) {
+      uint4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = base[e + u * stride];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w;
+      }
+    }
+    for (; e < region; e += stride) {
+      uint4 v = base[e];
+      acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+    }
+  }
+  if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x85ebca6bu && acc.w == 0xc2b2ae35u)
+    sink[blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void l2_rows_kernel(const uint4* __restrict__ buf,
+                                                           long region, int iters,
+                                                           uint4* __restrict__ sink) {
+  const int xcd = blockIdx.x % kXcds;
+  const unsigned local = blockIdx.x / kXcds;
+  const unsigned per_xcd = gridDim.x / kXcds;
+  const uint4* base = buf + (long)xcd * region;
+  const unsigned rows = (unsigned)(region / 16);          // 256-byte rows
+  const unsigned group = local * (kThreads / 16) + threadIdx.x / 16;
+  const unsigned groups = per_xcd * (kThreads / 16);
+  const int piece = threadIdx.x % 16;
+  // each group visits `rows / groups` rows per pass, in a scrambled order
+  const unsigned per_pass = rows / groups;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (int it = 0; it < iters; ++it) {
+    for (unsigned r0 = 0; r0 + kUnroll <= per_pass; r0 += kUnroll) {
+      uint4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const unsigned t = (r0 + u) * groups + group + (unsigned)it * 7919u;
+        const unsigned row = (t * 2654435761u) % rows;
+        v[u] = base[(long)row * 16 + piece];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w;
+      }
+    }
+  }
+  if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x85ebca6bu && acc.w == 0xc2b2ae35u)
+    sink[blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" __attribute__((visibility("default")))
+/* Launches one calibration pass on `stream`.
+ * buf: device buffer of 8 * region_bytes (one region per XCD); region_bytes a
+ * multiple of 4096. grid: workgroups (a multiple of 8). mode 0 or 1 as above.
+ * sink: device buffer of grid * 256 * 16 bytes (written only in the
+ * practically impossible case above). Returns 0, -1 on bad arguments, or the
+ * hipError_t of the launch. Bytes read per pass: mode 0: iters * 8 *
+ * region_bytes; mode 1: iters * 8 * 256 * (rows / groups) * groups with
+ * rows = region_bytes / 256 and groups = grid / 8 * 16. */
+int amtk_calib_l2_read(const void* buf, size_t region_bytes, int iters, int grid, int mode,
+                       void* sink, void* stream) {
+  if (!buf || !sink || region_bytes == 0 || region_bytes % 4096 || iters < 1 || grid < kXcds ||
+      grid % kXcds || (mode != 0 && mode != 1))
+    return -1;
+  const long region = (long)(region_bytes / sizeof(uint4));
+  if (mode == 1 && (region / 16) < (long)(grid / kXcds) * (kThreads / 16)) return -1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mode == 0)
+    l2_stream_kernel<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(buf), region, iters,
+                                                 static_cast<uint4*>(sink));
+  else
+    l2_rows_kernel<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(buf), region, iters,
+                                               static_cast<uint4*>(sink));
+  return (int)hipGetLastError();
+}

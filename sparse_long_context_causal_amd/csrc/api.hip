@@ -202,6 +202,11 @@ int amtk_topk_workspace(const amtk_attn_desc* attn, const amtk_support_desc* sup
   return AMTK_OK;
 }
 
+size_t amtk_workspace_bytes(const amtk_attn_desc* attn, const amtk_support_desc* sup) {
+  size_t b = 0;
+  return amtk_topk_workspace(attn, sup, &b) == AMTK_OK ? b : 0;
+}
+
 int topk_support(const amtk_attn_desc* attn, const amtk_support_desc* sup, const void* q,
                  const void* k, int32_t* idx, int32_t* count, float* mass, float* lse, void* ws,
                  size_t ws_bytes, void* stream) {

@@ -5,7 +5,7 @@ import numpy as np
 from tests.support_rules import check_row
 
 TOL_OUT = {"bf16": 2e-3, "f32": 1e-5}     # outputs on identical supports (max abs)
-TOL_LSE = {"bf16": 1e-4, "f32": 1e-5}     # per-head dense log-sum-exp (max abs)
+TOL_LSE = {"bf16": 1e-4, "f32": 1e-5}     # per-head log-sum-exp, dense or on a support (max abs)
 BAND = 1e-6                               # near-tie band around the k-th mass
 
 
@@ -51,5 +51,5 @@ def check_outputs_on_gpu_support(out, lse_s, oracle, rows, units, counts, key_bl
         worst = max(worst, err)
         assert err <= TOL_OUT[dtype], f"row {i}: max abs err {err}"
         if lse_s is not None:
-            assert np.max(np.abs(lse_s[:, i] - l_ref)) <= TOL_LSE[dtype] * 10, f"row {i} lse_s"
+            assert np.max(np.abs(lse_s[:, i] - l_ref)) <= TOL_LSE[dtype], f"row {i} lse_s"
     return worst

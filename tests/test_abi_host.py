@@ -49,6 +49,19 @@ def test_every_declared_symbol_is_exported(lib):
     assert ours == set(names), sorted(ours - set(names))
 
 
+def test_workspace_bytes_matches_the_status_form(lib):
+    for kw in (dict(), dict(n=1000, hq=32, hkv=8, d=128, k=82), dict(k=4, kb=64), dict(qb=64)):
+        a, s = _descs(**kw)
+        need = ctypes.c_size_t(0)
+        assert lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s), ctypes.byref(need)) == 0
+        assert need.value > 0
+        assert lib.amtk_workspace_bytes(ctypes.byref(a), ctypes.byref(s)) == need.value
+    for kw in (dict(n=0), dict(causal=0), dict(k=0), dict(kb=2)):
+        a, s = _descs(**kw)
+        assert lib.amtk_workspace_bytes(ctypes.byref(a), ctypes.byref(s)) == 0
+    assert lib.amtk_workspace_bytes(None, None) == 0
+
+
 def test_strerror_covers_codes(lib):
     for c in (0, -1, -2, -3, -4, -99):
         assert lib.amtk_strerror(c)

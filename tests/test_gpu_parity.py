@@ -14,6 +14,7 @@ import pytest
 
 from oracle import OracleLayer, IndexerOracle, tokens_of_blocks
 from synth import WORKLOADS, generate, random_inputs, round_bf16, sample_rows
+from tests.support_rules import check_row
 from tests.gpu_helpers import (BAND, TOL_LSE, TOL_OUT, check_outputs_on_gpu_support,
                                check_support_rows, upload)
 
@@ -297,7 +298,7 @@ def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block):
         o_ref, l_ref = layer.attention_on(i, toks)
         err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
         assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
-        assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
+        assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"], f"row {i} lse"
 
 
 # ------------------------------------------------ selection-block-shared support
@@ -389,7 +390,7 @@ def test_sparse_attn_blocks_oracle_supports(gpu_lib):
         if np.all(np.isneginf(r["lse_s"][i])):
             assert np.all(np.isneginf(lse[:, i])), f"row {i} lse"
         else:
-            assert np.max(np.abs(lse[:, i] - r["lse_s"][i])) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
+            assert np.max(np.abs(lse[:, i] - r["lse_s"][i])) <= TOL_LSE["bf16"], f"row {i} lse"
 
 
 def test_sparse_attn_blocks_unsorted_invalid_and_clamped(gpu_lib):
@@ -436,49 +437,67 @@ def test_sparse_attn_blocks_unsorted_invalid_and_clamped(gpu_lib):
         o_ref, l_ref = layer.attention_on(i, toks)
         err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
         assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
-        assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"] * 10, f"row {i} lse"
+        assert np.max(np.abs(lse[:, i] - l_ref)) <= TOL_LSE["bf16"], f"row {i} lse"
 
 
 # ------------------------------------------------------------ the workloads
-def _workload_check(amtk, name, rows_cap=None, n=None):
+_GEN_CACHE = {}
+
+
+def _generated(name):
+    """Each workload's inputs are generated once per test session (the 100K
+    layer takes seconds to build); only the latest one is kept."""
+    if name not in _GEN_CACHE:
+        _GEN_CACHE.clear()
+        _GEN_CACHE[name] = generate(WORKLOADS[name])
+    return _GEN_CACHE[name]
+
+
+def _workload_check(amtk, name, k=None):
+    """The whole seeded oracle row sample of a workload (every row at 512 and
+    4096 tokens, 256 rows at 32K, 128 at 100K), in the launch configuration
+    the benchmark times (oracle_prefill): per-head LSE, selected masses,
+    supports by the near-tie rule, outputs on the GPU's own supports, and
+    every surviving planted needle of a checked row selected."""
     w = WORKLOADS[name]
-    x = generate(w, n=n)
-    rows = sample_rows(w, n=n)
-    if rows_cap is not None and rows.size > rows_cap:
-        rows = rows[np.linspace(0, rows.size - 1, rows_cap).astype(int)]
-    res, layer = _full_check(amtk, x, w.dtype, w.k, w.key_block, rows=rows)
-    # every surviving needle (owner row, key) in the checked rows is selected
+    x = _generated(name)
+    rows = sample_rows(w)
+    k = w.k if k is None else k
+    res, layer = _full_check(amtk, x, w.dtype, k, w.key_block, rows=rows)
     owners = x["owner"]
+    lost = []
+    n_needles = 0
     for i in rows:
         mine = np.nonzero(owners == i)[0]
+        n_needles += mine.size
         sel = set(res["idx"][i][: res["count"][i]].tolist())
-        assert set(mine.tolist()) <= sel, f"row {i} lost a needle"
-    return res
+        if not set(mine.tolist()) <= sel:
+            lost.append(int(i))
+    assert not lost, f"rows {lost[:8]} lost a needle"
+    return res, rows, n_needles
 
 
 def test_workload_tiny_fp32_512_all_rows(gpu_lib):
-    _workload_check(gpu_lib, "tiny_fp32_512")
+    _, rows, nn = _workload_check(gpu_lib, "tiny_fp32_512")
+    assert rows.size == 512 and nn > 0
 
 
-def test_workload_mid_bf16_4k(gpu_lib):
-    _workload_check(gpu_lib, "mid_bf16_4k", rows_cap=512)
+def test_workload_mid_bf16_4k_all_rows(gpu_lib):
+    _, rows, nn = _workload_check(gpu_lib, "mid_bf16_4k")
+    assert rows.size == 4096 and nn > 0
 
 
-def test_workload_long_bf16_32k_sampled(gpu_lib):
-    _workload_check(gpu_lib, "long_bf16_32k", rows_cap=48)
+def test_workload_long_bf16_32k_sample(gpu_lib):
+    _, rows, _ = _workload_check(gpu_lib, "long_bf16_32k")
+    assert rows.size == 256
 
 
 @pytest.mark.parametrize("k", [512, 1024, 2048])
-def test_workload_vlong_bf16_100k_sampled(gpu_lib, k):
-    import torch
-    w = WORKLOADS["vlong_bf16_100k"]
-    x = generate(w)
-    rows = sample_rows(w)[::8]
-    res = _run_oracle_prefill(gpu_lib, x, "bf16", k)
-    layer = OracleLayer(x["q"], x["k"], x["v"])
-    check_support_rows(res["idx"], res["count"], layer, rows, k)
-    check_outputs_on_gpu_support(res["out"], None, layer, rows, res["idx"], res["count"], 1,
-                                 "bf16")
+def test_workload_vlong_bf16_100k_sample(gpu_lib, k):
+    """The budget sweep of the 100K layer; oracle_prefill runs the windowed
+    gather here (13 key windows)."""
+    _, rows, _ = _workload_check(gpu_lib, "vlong_bf16_100k", k=k)
+    assert rows.size == 128
 
 
 # ----------------------------------------------------------------- indexer
@@ -527,21 +546,31 @@ def test_indexer_zero_queries_tie_by_block_size(gpu_lib):
             assert idx[i][:2].tolist() == [0, 1]          # full blocks outweigh the partial one
 
 
-def test_workload_indexer_bf16_32k_sampled(gpu_lib):
+def test_workload_indexer_bf16_32k_sample(gpu_lib):
+    """The indexer workload on its whole seeded row sample (256 rows): the
+    indexer's top-16 key blocks by the near-tie rule, their block masses,
+    and the gather on them (one pass and windowed) against the oracle."""
     import torch
     amtk = gpu_lib
     w = WORKLOADS["indexer_bf16_32k"]
-    x = generate(w)
-    rows = sample_rows(w)[::4]
-    idx, cnt, _ = _indexer_run(amtk, x["q_idx"], x["k_idx"], w.k, w.key_block)
+    x = _generated("indexer_bf16_32k")
+    rows = sample_rows(w)
+    assert rows.size == 256
+    idx, cnt, mass = _indexer_run(amtk, x["q_idx"], x["k_idx"], w.k, w.key_block)
     ix = IndexerOracle(x["q_idx"], x["k_idx"])
-    check_support_rows(idx, cnt, None, rows, w.k,
-                       scores=lambda i: (lambda r: (r["score"], r["kth"]))(ix.row(int(i), w.k, 64)))
+    for i in rows:
+        r = ix.row(int(i), w.k, w.key_block)
+        ok, msg, _ = check_row(idx[i], cnt[i], r["score"], r["kth"], w.k, BAND)
+        assert ok, f"row {i}: {msg}"
+        sel = idx[i][: cnt[i]]
+        want = r["score"][sel]
+        assert np.all(np.abs(mass[i][: cnt[i]] - want) <= 1e-7 + 2e-4 * want), f"mass row {i}"
     d = upload(x, "bf16")
     ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
-    out, _ = amtk.sparse_attn(d["q"], d["k"], d["v"], ti, tc, 64)
+    out, lse_s = amtk.sparse_attn(d["q"], d["k"], d["v"], ti, tc, 64, want_lse=True)
     layer = OracleLayer(x["q"], x["k"], x["v"])
-    check_outputs_on_gpu_support(out.cpu().numpy(), None, layer, rows, idx, cnt, 64, "bf16")
+    check_outputs_on_gpu_support(out.cpu().numpy(), lse_s.cpu().numpy(), layer, rows, idx, cnt,
+                                 64, "bf16")
     # the windowed gather (four 8192-token windows) on the same supports
     out_w, _ = amtk.sparse_attn_windowed(d["q"], d["k"], d["v"], ti, tc, 64)
     torch.cuda.synchronize()
