@@ -126,10 +126,9 @@ def l2_read_ceiling(regions_mb=(1, 2, 3), mode=0, grid=2048, pass_bytes=8e9, rep
             iters = max(1, int(pass_bytes / (8 * region)))
             nbytes = iters * 8 * region
         else:
-            rows, groups = region // 256, grid // 8 * 16
-            per_group = (rows // groups) // 8 * 8
-            iters = max(1, int(pass_bytes / (8 * 256 * per_group * groups)))
-            nbytes = iters * 8 * 256 * per_group * groups
+            per_iter = grid * 16 * 64 * 256          # 64 rows per 16-lane group
+            iters = max(1, int(pass_bytes / per_iter))
+            nbytes = iters * per_iter
         times = []
         for r in range(reps + 1):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -174,6 +174,36 @@ int sparse_attn_windowed(const amtk_attn_desc* attn, int32_t key_block, int32_t 
                          const int32_t* count, float* o, float* lse_sparse, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* Bytes of the static device scratch array of sparse_attn_windowed_static
+ * (one copy per GPU, held until the process ends). */
+#define AMTK_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * sparse_attn_windowed_static - sparse_attn_windowed for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It takes no workspace: the windowed
+ * gather's scratch (window starts of every row, and the running LSE when
+ * lse_sparse is NULL) lives in a static device array of
+ * AMTK_STATIC_SCRATCH_BYTES on each GPU. The call allocates and frees
+ * nothing; the result is exactly that of sparse_attn_windowed (same kernels).
+ * Arguments and validation as sparse_attn_windowed, without ws / ws_bytes.
+ * The array of the CURRENT device (hipGetDevice) is used, so the current
+ * device must be the device of `stream`; its address is resolved at the
+ * first call on each device.
+ * Limit: the layer's scratch, amtk_sparse_attn_workspace() = n * 4 * (key
+ * windows + 1) + hq * n * 4 bytes (rounded to 256), must fit the array:
+ * n up to about 160K tokens at hq = 32. Larger layers return
+ * AMTK_E_WORKSPACE before anything is launched.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs clearing: every word a call reads, the call
+ * writes first). Calls that overlap on one GPU (other streams, other host
+ * threads) race on the array and must be serialised by the caller.
+ */
+int sparse_attn_windowed_static(const amtk_attn_desc* attn, int32_t key_block,
+                                int32_t max_units, const void* q, const void* k, const void* v,
+                                const int32_t* idx, const int32_t* count, float* o,
+                                float* lse_sparse, void* stream);
+
 /*
  * sparse_attn_blocks - attention of each selection block's queries on the
  * block's shared support, the keys gathered once per block.

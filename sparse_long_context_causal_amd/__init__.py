@@ -191,6 +191,31 @@ def sparse_attn_windowed(q, k, v, idx, count, key_block: int = 1, scale: Optiona
     return out, lse
 
 
+def sparse_attn_windowed_static(q, k, v, idx, count, key_block: int = 1,
+                                scale: Optional[float] = None, want_lse: bool = False, out=None):
+    """sparse_attn_windowed with its scratch in the library's static device
+    array (no workspace; the C call allocates nothing). Outputs are allocated
+    here unless `out` is given. Returns (out [N,Hq,d] fp32, lse_sparse [Hq,N]
+    or None)."""
+    torch = _torch()
+    _check_dev(q, k, v, idx, count)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    if idx.dtype != torch.int32 or count.dtype != torch.int32:
+        raise TypeError("idx and count must be int32")
+    ad = attn_desc(q, k, scale)
+    n, hq, d = q.shape
+    if idx.dim() != 2 or idx.shape[0] != n or count.shape != (n,):
+        raise ValueError("idx must be [N, max_units] and count [N]")
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=q.device) if want_lse else None
+    _call("sparse_attn_windowed_static", ctypes.byref(ad), int(key_block), int(idx.shape[1]),
+          _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(count), _ptr(out), _ptr(lse),
+          _stream(q.device))
+    return out, lse
+
+
 def sparse_attn_blocks(q, k, v, idx, count, query_block: int = 64, key_block: int = 1,
                        scale: Optional[float] = None, want_lse: bool = False, out=None):
     """Attention of each selection block of query_block rows on the support in

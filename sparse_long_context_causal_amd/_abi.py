@@ -12,6 +12,7 @@ AMTK_E_INVALID = -1
 AMTK_E_UNSUPPORTED = -2
 AMTK_E_WORKSPACE = -3
 AMTK_E_HIP = -4
+AMTK_STATIC_SCRATCH_BYTES = 32 << 20
 AMTK_BF16 = 0
 AMTK_F32 = 1
 
@@ -40,6 +41,8 @@ SIGNATURES = {
     "topk_support": (ctypes.c_int, [_A, _S, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "topk_support_stage": (ctypes.c_int, [_A, _S, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sparse_attn": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sparse_attn_windowed_static": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                                   _P]),
     "sparse_attn_blocks": (ctypes.c_int, [_A, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "amtk_sparse_attn_workspace": (ctypes.c_int, [_A, ctypes.POINTER(_SZ)]),
     "sparse_attn_windowed": (ctypes.c_int, [_A, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,

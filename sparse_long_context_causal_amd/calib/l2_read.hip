@@ -22,6 +22,7 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
+constexpr unsigned kRowsPerPass = 64;   // rows one 16-lane group reads per pass (mode 1)
 
 __global__ __launch_bounds__(kThreads) void l2_stream_kernel(const uint4* __restrict__ buf,
                                                              long region, int iters,
@@ -57,21 +58,18 @@ __global__ __launch_bounds__(kThreads) void l2_rows_kernel(const uint4* __restri
                                                            uint4* __restrict__ sink) {
   const int xcd = blockIdx.x % kXcds;
   const unsigned local = blockIdx.x / kXcds;
-  const unsigned per_xcd = gridDim.x / kXcds;
   const uint4* base = buf + (long)xcd * region;
   const unsigned rows = (unsigned)(region / 16);          // 256-byte rows
   const unsigned group = local * (kThreads / 16) + threadIdx.x / 16;
-  const unsigned groups = per_xcd * (kThreads / 16);
   const int piece = threadIdx.x % 16;
-  // each group visits `rows / groups` rows per pass, in a scrambled order
-  const unsigned per_pass = rows / groups;
+  // each group reads kRowsPerPass rows per pass at scrambled positions
   uint4 acc = make_uint4(0, 0, 0, 0);
   for (int it = 0; it < iters; ++it) {
-    for (unsigned r0 = 0; r0 + kUnroll <= per_pass; r0 += kUnroll) {
+    for (unsigned r0 = 0; r0 < kRowsPerPass; r0 += kUnroll) {
       uint4 v[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const unsigned t = (r0 + u) * groups + group + (unsigned)it * 7919u;
+        const unsigned t = (group * kRowsPerPass + r0 + u) + (unsigned)it * 7919u;
         const unsigned row = (t * 2654435761u) % rows;
         v[u] = base[(long)row * 16 + piece];
       }
@@ -94,15 +92,14 @@ extern "C" __attribute__((visibility("default")))
  * sink: device buffer of grid * 256 * 16 bytes (written only in the
  * practically impossible case above). Returns 0, -1 on bad arguments, or the
  * hipError_t of the launch. Bytes read per pass: mode 0: iters * 8 *
- * region_bytes; mode 1: iters * 8 * 256 * (rows / groups) * groups with
- * rows = region_bytes / 256 and groups = grid / 8 * 16. */
+ * region_bytes; mode 1: iters * grid * 16 * 64 * 256 (64 rows of 256 bytes per
+ * 16-lane group and pass). */
 int amtk_calib_l2_read(const void* buf, size_t region_bytes, int iters, int grid, int mode,
                        void* sink, void* stream) {
   if (!buf || !sink || region_bytes == 0 || region_bytes % 4096 || iters < 1 || grid < kXcds ||
       grid % kXcds || (mode != 0 && mode != 1))
     return -1;
   const long region = (long)(region_bytes / sizeof(uint4));
-  if (mode == 1 && (region / 16) < (long)(grid / kXcds) * (kThreads / 16)) return -1;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (mode == 0)
     l2_stream_kernel<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(buf), region, iters,

@@ -188,6 +188,11 @@ int indexer_shape(int64_t n, int32_t d_idx, int32_t dtype, float scale, LayerSha
 
 }  // namespace
 
+namespace amtk {
+int validate_attn(const amtk_attn_desc* a, LayerShape* s) { return check_attn(a, s); }
+int record_hip_error(hipError_t e) { return hip_fail(e); }
+}  // namespace amtk
+
 #pragma GCC visibility push(default)
 extern "C" {
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "amtk.h"
+
 namespace amtk {
 
 enum ElemType { kBF16 = 0, kF32 = 1 };
@@ -122,6 +124,13 @@ hipError_t launch_kl_distill(const LayerShape& s, int d_idx, float idx_scale, co
                              const void* k, const void* q_idx, const void* k_idx,
                              const float* lse, const float* lse_t, float* kl_row, float* loss,
                              float* dq, float* dk, float* dk_part, hipStream_t stream);
+
+// Host-side helpers of the entry points (api.hip): the layer descriptor's
+// validation (AMTK_OK or an AMTK_E_* code, *s filled on success), and the
+// bookkeeping of a failed HIP call (keeps e for amtk_last_hip_error on this
+// thread, returns AMTK_E_HIP).
+int validate_attn(const amtk_attn_desc* a, LayerShape* s);
+int record_hip_error(hipError_t e);
 
 bool pass_shape_supported(const LayerShape& s);
 bool sparse_shape_supported(const LayerShape& s);

@@ -214,6 +214,28 @@ def test_indexer_prefill_validation(lib):
         assert ok(s_fused, args=bad) == -1
 
 
+def test_static_windowed_validation(lib):
+    from sparse_long_context_causal_amd import _abi
+    f = lib.sparse_attn_windowed_static
+    ok = lambda a, kb=1, mu=16, ptrs=None: f(ctypes.byref(a), kb, mu, *(ptrs or [FAKE] * 7), None,
+                                            None)
+    big = _abi.AttnDesc(400000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    assert ok(big) == -3                                # more scratch than the static array
+    need = ctypes.c_size_t(0)
+    assert lib.amtk_sparse_attn_workspace(ctypes.byref(big), ctypes.byref(need)) == 0
+    assert need.value > _abi.AMTK_STATIC_SCRATCH_BYTES
+    fits = _abi.AttnDesc(150000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    assert lib.amtk_sparse_attn_workspace(ctypes.byref(fits), ctypes.byref(need)) == 0
+    assert need.value <= _abi.AMTK_STATIC_SCRATCH_BYTES
+    assert ok(fits, kb=2) == -2
+    assert ok(fits, mu=0) == -1
+    for j in range(7):                                  # q, k, v, idx, count, o, (lse optional)
+        ptrs = [FAKE] * 7
+        ptrs[j] = None if j < 6 else ctypes.c_void_p(0x100002)
+        assert ok(fits, ptrs=ptrs) == -1, j
+    assert ok(_abi.AttnDesc(1000, 32, 8, 128, _abi.AMTK_BF16, 0, 0.0)) == -2
+
+
 def test_diagnostics_validation(lib):
     odd = ctypes.c_void_p(0x100002)
     assert lib.captured_mass(0, 8, FAKE, FAKE, FAKE, None) == -1
