@@ -1,6 +1,6 @@
 // KL-distillation loss of the head-collapsed indexer against the oracle's
-// attention mass, with its gradients, in one streaming pass over the causal
-// triangle (the N x N matrices are never stored).
+// attention mass, with its gradients, streamed over the causal triangle; no
+// N x N matrix, and no array of that size, is stored.
 //
 // Method: gist.science page on arXiv 2606.07703, "Technischer Bericht"
 // section 2.2: the indexer is trained by KL divergence from the dense
@@ -14,9 +14,9 @@
 // Both log-sum-exps come first from pass 1 (teacher per head, student with
 // one head of d_idx).
 //
-// kl_tile_kernel (bf16, d = 128, 8 KV heads x 4 query heads, d_idx = 64):
-// one workgroup of 8 waves per 32-query tile, wave g = KV head g, key tiles
-// streamed as in pass 2. Per key tile:
+// kl_tile_kernel (bf16, d = 128, 8 KV heads x 4 query heads, d_idx = 64),
+// query-major: one workgroup of 8 waves per 32-query tile, wave g = KV head
+// g, key tiles streamed as in pass 2. Per key tile:
 //  * every wave scores its 4 heads (32x32x16 MFMAs), turns them into
 //    probabilities with the dense LSE and sums them; the 8 partial tiles
 //    meet in LDS and the workgroup assembles the teacher tile P[key][query];
@@ -25,12 +25,10 @@
 //    half of the keys each, and accumulate dq^T[d][query] += k_idx^T dS^T for
 //    their 32 of the 64 dimensions (A = k_idx columns by transposing LDS
 //    reads, B = the lane's own dS); dS is split into bf16 hi + lo, so the
-//    products keep about 16 significant bits;
-//  * waves 2 and 3 compute the student tile the other way round
-//    (lane = key), dS, and this tile pair's dk^T[d][key] = q_idx^T dS
-//    for their 32 dimensions, written to the workspace;
-// kl_dk_reduce_kernel then sums, per key tile, the pair partials over the
-// query tiles in a fixed order (deterministic), and kl_loss_kernel the mean.
+//    products keep about 16 significant bits.
+// kl_dk_kernel (key-major, below) computes the key gradient per KV group,
+// kl_dk_sum_kernel adds the 8 groups per key in a fixed order, and
+// kl_loss_kernel takes the mean; every sum has a fixed order (deterministic).
 //
 // The k_idx / q_idx tiles (32 rows of 128 bytes) sit in LDS with d-chunk x
 // of row R at position x ^ f(R), f(R) = 2(R & 3) + ((R >> 2) & 1): the
@@ -145,7 +143,7 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ QI,
     const bf16_t* __restrict__ KI, const float* __restrict__ lse, const float* __restrict__ lse_t,
     int n, float c, float ct, float* __restrict__ kl_row, float* __restrict__ dq,
-    float* __restrict__ dk_part, float grad_scale) {
+    float grad_scale) {
   extern __shared__ __align__(1024) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
     const unsigned u = 2u * (G16 & 1u) + (cc >> 1), sw = 2u * e + (G16 >> 1);
     tr_off = 128u * (4u * (G16 >> 1) + e) + 8u * (cc & 1u) + 16u * (u ^ sw);
   }
-  const int dt = wave & 1;   // the d tile of waves 0-3
+  const int dt = wave & 1;   // the d tile of waves 0 and 1
 
   // dq^T accumulators of waves 0 and 1 live in LDS between key tiles
   // (registers j*4 .. j*4+3 of lane l at float4 slot (wave, j, l))
@@ -263,13 +261,13 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
       ptile[key * kKlPitch + qq] = p * (1.0f / (float)kKlHq);
     }
     barrier_lds();   // P visible
-    if (wave >= 4) continue;
+    if (wave >= 2) continue;
 
     // ---- student tile, dS = Q - P, and the gradient products
     const uint32_t kb = base + kKlKidx + 4096u * (unsigned)(kt & 1);
     const uint32_t qb = base + kKlQidx;
     const float* lse_tl = reinterpret_cast<const float*>(smem + kKlLseT);
-    if (wave < 2) {
+    {
       // lane = query col: t^T[key][query] = k_idx q_idx^T
       f32x16 t = f32x16{};
 #pragma unroll
@@ -313,50 +311,6 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
                                                         __builtin_bit_cast(bf16x8, bl[ks]), dqacc, 0, 0, 0);
       }
       dq_store(dq_lds, dqacc);
-    } else {
-      // lane = key col: t[query][key] = q_idx k_idx^T
-      f32x16 t = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 kf, qf;
-        read_idx_frag2((kb + frag_off) ^ (32u * s), (qb + frag_off) ^ (32u * s), kf, qf);
-        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf),
-                                                    __builtin_bit_cast(bf16x8, kf), t, 0, 0, 0);
-      }
-      u32x4 bh[2], bl[2];
-#pragma unroll
-      for (int r2 = 0; r2 < 16; r2 += 2) {
-        float dsv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = r2 + u, qq = acc_row(r, hf);
-          const float p = ptile[col * kKlPitch + qq];
-          const float x = fmaf(t[r], ct, -lse_tl[qq]);
-          const bool live = q0 + qq < n && !(diag && col > qq);
-          dsv[u] = live ? fast_exp2(x) - p : 0.f;
-        }
-        const unsigned h = pack2_bf16(dsv[0], dsv[1]);
-        bh[r2 >> 3][(r2 & 7) >> 1] = h;
-        bl[r2 >> 3][(r2 & 7) >> 1] =
-            pack2_bf16(dsv[0] - __uint_as_float(h << 16), dsv[1] - __uint_as_float(h & 0xffff0000u));
-      }
-      u32x2 tr[4];
-      read_idx_tr((qb + tr_off) ^ (64u * (unsigned)dt), tr);   // q_idx^T, rows = queries
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 av = {tr[2 * ks].x, tr[2 * ks].y, tr[2 * ks + 1].x, tr[2 * ks + 1].y};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                      __builtin_bit_cast(bf16x8, bh[ks]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                      __builtin_bit_cast(bf16x8, bl[ks]), acc, 0, 0, 0);
-      }
-      // dk^T[d][key] of this (query tile, key tile) pair: lane = key col,
-      // register r = d 32 dt + 8(r/4) + 4 hf + r%4
-      float* dst = dk_part + ((size_t)qt * (qt + 1) / 2 + kt) * (32 * kKlDi) + col * kKlDi + 32 * dt + 4 * hf;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(dst + 8 * j) = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
     }
   }
   // ---- per-row KL (waves 0 and 1) and dq (waves 0, 1)
@@ -376,43 +330,252 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
   }
 }
 
-// dk[j] = grad_scale * sum over query tiles qt >= kt of the pair partials,
-// in increasing qt (one workgroup per key tile kt).
-__global__ __launch_bounds__(256) void kl_dk_reduce_kernel(const float* __restrict__ dk_part,
-                                                           int n, float grad_scale,
-                                                           float* __restrict__ dk) {
-  const int kt = (int)blockIdx.x;
+// ------------------------------------------------------ key gradient
+// dL/dk_idx[j] = (tau_idx/N) sum_{i>=j} (Q_ij - P_ij) q_idx[i] is linear in
+// the teacher's head sum, P_ij = (1/Hq) sum_g sum_{h in g} p_h(i,j), so it
+// splits over the KV groups g:
+//   dk[j] = (tau_idx/N) sum_g C_g[j],
+//   C_0[j] = sum_i (Q_ij - S_0(i,j)/Hq) q_idx[i],  C_g[j] = -sum_i S_g(i,j)/Hq q_idx[i] (g > 0),
+// with S_g(i,j) = sum of p_h(i,j) over the 4 query heads of group g. Each
+// group's share needs only that group's K and Q heads, so no workgroup
+// exchanges partial masses with another, and the per-group sums (8 x n x
+// d_idx floats) are added per key in increasing g by kl_dk_sum_kernel.
+//
+// kl_dk_kernel: one workgroup of 8 waves per (256 keys, KV group g), wave w
+// owning key tile kb*8 + w. Workgroups are numbered so that XCD g serves
+// group g. A wave holds its key tile of K (KV head g) in registers as the MFMA
+// B operand and walks the query tiles from its own key tile to the last; the
+// workgroup streams each query tile's 4 query heads (32 rows x 256 B each),
+// the tile's q_idx rows, dense LSE and student LSE into LDS once for all 8
+// waves (double buffered, one barrier per query tile). Per query tile a wave:
+//  * scores S[query][key] = Q_h K^T (32x32x16 MFMAs, A = query rows from LDS,
+//    lane = key, register r = query acc_row(r)), turns each head into
+//    probabilities with the dense LSE and sums the 4 heads in registers;
+//  * (group 0) scores the student t[query][key] = q_idx k_idx^T and adds Q;
+//  * accumulates C^T[d][key] += q_idx^T[d][query] v[query][key] for both
+//    32-wide d tiles, with v = (Q -) S/Hq split into bf16 hi + lo and the
+//    transposed q_idx operand read to match the score layout's query order.
+constexpr int kDkWaves = 8;                          // key tiles per workgroup
+constexpr unsigned kDkQ = 0;                         // 4 query heads x 8 KiB
+constexpr unsigned kDkQidx = 4 * 8192;               // q_idx tile (4 KiB)
+constexpr unsigned kDkLse = kDkQidx + 4096;          // dense LSE x log2e [4][32]
+constexpr unsigned kDkLseT = kDkLse + 512;           // student LSE x log2e [32]
+constexpr unsigned kDkBuf = 40960;                   // one query tile's buffer
+constexpr unsigned kDkLds = 2 * kDkBuf;
+
+// One 1 KiB piece (instruction c: rows 4c .. 4c+3) of a 32-row x 256-byte
+// tile of head `head` of X [n][heads][128] (rows r0 ..), laid out as the key
+// tiles of KLane: chunk j of row R at 16-byte position R*16 + (j ^ (R & 15)).
+// Rows past n repeat row n-1.
+__device__ __forceinline__ void dk_dma_piece(const bf16_t* X, int heads, int head, int r0, int n,
+                                             int c, unsigned char* slot, int lane) {
+  const int row = 4 * c + (lane >> 4);
+  const int rr = min(r0 + row, n - 1);
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(X + ((size_t)rr * heads + head) * kKlD) +
+                             16 * ((lane & 15) ^ (row & 15));
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(slot + 1024 * c), 16, 0, 0);
+}
+
+__global__ __launch_bounds__(512) void kl_dk_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ QI,
+    const bf16_t* __restrict__ KI, const float* __restrict__ lse, const float* __restrict__ lse_t,
+    int n, float c, float ct, float* __restrict__ cpart) {
+  extern __shared__ __align__(1024) unsigned char smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hf = lane >> 5, col = lane & 31;
+  const int g = (int)(blockIdx.x % kKlHkv);          // XCD g serves group g
+  const int kb = (int)(blockIdx.x / kKlHkv);         // longest rows first
   const int ntiles = (n + 31) >> 5;
-  const int e = (int)threadIdx.x * 8;   // 8 of the tile's 32 x 64 values
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  // four query tiles' partials in flight per step, summed in query-tile order
-  int qt = kt;
-  for (; qt + 4 <= ntiles; qt += 4) {
-    float4 x[4], y[4];
+  const int kt = kb * kDkWaves + wave;               // this wave's key tile
+  const int k0 = kt << 5;
+  const int qfirst = kb * kDkWaves;                  // first query tile the workgroup visits
+  const uint32_t base = lds_addr(smem);
+
+  // ---- the wave's key tile of K (B operand) through a temporary LDS slot
+  uint4 kc[kKlNc];
+  {
+    KLane<bf16_t, kKlD> kl;
+    kl.init(lane, kKlHkv);
+    unsigned char* tmp = smem + 8192u * (unsigned)wave;
+    kl.issue(K, n, kKlHkv, g, min(k0, ((n - 1) >> 5) << 5), tmp);
+    wait_vmem_all();
+    kl.read(tmp, kc);
+  }
+  // the key tile's k_idx rows (B operand of the student scores, group 0):
+  // lane (key col, half hf) holds d = 16 s + 8 hf + [0, 8) for s = 0..3
+  uint4 kif[4];
+  {
+    const int krow = min(k0 + col, n - 1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t t = (size_t)(qt + u);
-      const float4* src = reinterpret_cast<const float4*>(dk_part + (t * (t + 1) / 2 + kt) * (32 * kKlDi) + e);
-      x[u] = src[0];
-      y[u] = src[1];
+    for (int s = 0; s < 4; ++s)
+      kif[s] = *reinterpret_cast<const uint4*>(KI + (size_t)krow * kKlDi + 16 * s + 8 * hf);
+  }
+  barrier_lds();   // temporary slots free
+
+  // ---- streaming of query tiles (work split over the waves):
+  //  waves 0-7: 4 pieces each of the 4 heads' Q tiles (wave w: head w/2,
+  //             pieces 4(w%2) .. 4(w%2)+3);
+  //  waves 0-3: 8 q_idx rows each; wave 4: dense LSE; wave 5: student LSE
+  //             (both through registers, scaled by log2 e, written to LDS
+  //             before the next barrier).
+  const unsigned drow = 8u * (unsigned)wave + ((unsigned)lane >> 3);
+  const unsigned dpiece = 16u * (((unsigned)lane & 7u) ^ idx_swizzle(drow));
+  float lse_reg[2] = {0.f, 0.f};
+  auto issue_tile = [&](int qt) {
+    unsigned char* buf = smem + kDkBuf * (unsigned)(qt & 1);
+    const int q0 = qt << 5;
+    const int hh = wave >> 1;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      dk_dma_piece(Q, kKlHq, g * kKlG + hh, q0, n, 4 * (wave & 1) + p, buf + kDkQ + 8192u * hh, lane);
+    if (wave < 4) {
+      const int row = min(q0 + (int)drow, n - 1);
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(QI) + (size_t)row * (kKlDi * 2) + dpiece;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + kDkQidx + 1024u * wave), 16, 0, 0);
+    } else if (wave == 4) {
+      // lane l: heads (l >> 5) and 2 + (l >> 5), query q0 + l % 32
+      const int row = min(q0 + col, n - 1);
+      lse_reg[0] = lse[(size_t)(g * kKlG + hf) * n + row];
+      lse_reg[1] = lse[(size_t)(g * kKlG + 2 + hf) * n + row];
+    } else if (wave == 5) {
+      lse_reg[0] = lse_t[min(q0 + col, n - 1)];
+    }
+  };
+  auto publish_regs = [&](int qt) {   // after this wave's loads of tile qt landed
+    float* buf = reinterpret_cast<float*>(smem + kDkBuf * (unsigned)(qt & 1));
+    if (wave == 4) {
+      buf[kDkLse / 4 + 32 * hf + col] = lse_reg[0] * kLog2e;
+      buf[kDkLse / 4 + 32 * (2 + hf) + col] = lse_reg[1] * kLog2e;
+    } else if (wave == 5 && hf == 0) {
+      buf[kDkLseT / 4 + col] = lse_reg[0] * kLog2e;
+    }
+  };
+
+  // operand addresses in the index tiles (as in kl_tile_kernel)
+  const unsigned fr = (unsigned)col;
+  const uint32_t frag_off = 128u * fr + 16u * ((unsigned)hf ^ ((fr >> 2) & 1u)) + 32u * (fr & 3u);
+  uint32_t tr_off;
+  {
+    const unsigned G16 = (unsigned)lane >> 4, e = ((unsigned)lane >> 2) & 3u, cc = (unsigned)lane & 3u;
+    const unsigned u = 2u * (G16 & 1u) + (cc >> 1), sw = 2u * e + (G16 >> 1);
+    tr_off = 128u * (4u * (G16 >> 1) + e) + 8u * (cc & 1u) + 16u * (u ^ sw);
+  }
+  KLane<bf16_t, kKlD> ql;   // read offsets of the Q tiles (same layout as key tiles)
+  ql.init(lane, kKlHq);
+
+  f32x16 cacc[2] = {f32x16{}, f32x16{}};   // C^T[32 dt + acc_row][key col]
+  const bool active_wave = kt < ntiles;
+  const int key = k0 + col;
+
+  issue_tile(qfirst);
+  for (int qt = qfirst; qt < ntiles; ++qt) {
+    wait_vmem_all();                 // this wave's pieces and register loads of tile qt
+    publish_regs(qt);
+    barrier_lds();                   // tile qt complete; tile qt-1 no longer read
+    if (qt + 1 < ntiles) issue_tile(qt + 1);
+    if (!active_wave || qt < kt) continue;
+    const unsigned char* buf = smem + kDkBuf * (unsigned)(qt & 1);
+    const float* lsel = reinterpret_cast<const float*>(buf + kDkLse);
+    const float* lsetl = reinterpret_cast<const float*>(buf + kDkLseT);
+    const int q0 = qt << 5;
+    // ---- teacher: the group's 4 heads, summed
+    float psum[16];
+#pragma unroll
+    for (int h = 0; h < kKlG; ++h) {
+      uint4 qc[kKlNc];
+      ql.read(buf + kDkQ + 8192u * h, qc);
+      f32x16 a;
+      score_tile<bf16_t, kKlNc>(a, qc, kc);   // S[query][key]: lane = key, r = query
+      float bias[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 b4 = *reinterpret_cast<const float4*>(lsel + 32 * h + 8 * j + 4 * hf);
+        bias[4 * j] = b4.x; bias[4 * j + 1] = b4.y; bias[4 * j + 2] = b4.z; bias[4 * j + 3] = b4.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(a[r], c, -bias[r]));
+        psum[r] = h == 0 ? e : psum[r] + e;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- v = (Q -) S/Hq on the live pairs (key <= query < n)
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = -psum[r] * (1.0f / (float)kKlHq);
+    const uint32_t qb = base + kDkBuf * (unsigned)(qt & 1) + kDkQidx;
+    if (g == 0) {
+      f32x16 t = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 qf;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(qf) : "v"((qb + frag_off) ^ (32u * s)) : "memory");
+        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf),
+                                                    __builtin_bit_cast(bf16x8, kif[s]), t, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 b4 = *reinterpret_cast<const float4*>(lsetl + 8 * j + 4 * hf);
+        const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[4 * j + u] += fast_exp2(fmaf(t[4 * j + u], ct, -bt[u]));
+      }
+    }
+    u32x4 bh[2], bl[2];
+#pragma unroll
+    for (int r2 = 0; r2 < 16; r2 += 2) {
+      float dsv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = r2 + u, qq = q0 + acc_row(r, hf);
+        dsv[u] = (qq < n && key <= qq) ? v[r] : 0.f;
+      }
+      const unsigned h = pack2_bf16(dsv[0], dsv[1]);
+      bh[r2 >> 3][(r2 & 7) >> 1] = h;
+      bl[r2 >> 3][(r2 & 7) >> 1] =
+          pack2_bf16(dsv[0] - __uint_as_float(h << 16), dsv[1] - __uint_as_float(h & 0xffff0000u));
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a.x += x[u].x; a.y += x[u].y; a.z += x[u].z; a.w += x[u].w;
-      b.x += y[u].x; b.y += y[u].y; b.z += y[u].z; b.w += y[u].w;
+    for (int dt = 0; dt < 2; ++dt) {
+      u32x2 tr[4];
+      read_idx_tr((qb + tr_off) ^ (64u * (unsigned)dt), tr);   // q_idx^T, rows = queries
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 av = {tr[2 * ks].x, tr[2 * ks].y, tr[2 * ks + 1].x, tr[2 * ks + 1].y};
+        cacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, bh[ks]), cacc[dt], 0, 0, 0);
+        cacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, bl[ks]), cacc[dt], 0, 0, 0);
+      }
     }
   }
-  for (; qt < ntiles; ++qt) {
-    const float4* src = reinterpret_cast<const float4*>(dk_part + ((size_t)qt * (qt + 1) / 2 + kt) * (32 * kKlDi) + e);
-    const float4 x = src[0], y = src[1];
+  // ---- this group's C[key][d] for the wave's key tile
+  if (active_wave && key < n) {
+    float* dst = cpart + ((size_t)g * n + key) * kKlDi + 4 * hf;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * j) =
+            make_float4(cacc[dt][4 * j], cacc[dt][4 * j + 1], cacc[dt][4 * j + 2], cacc[dt][4 * j + 3]);
+  }
+}
+
+// dk[j][d] = grad_scale * sum over the 8 KV groups of C_g[j][d], in
+// increasing g.
+__global__ __launch_bounds__(256) void kl_dk_sum_kernel(const float* __restrict__ cpart, int n,
+                                                        float grad_scale, float* __restrict__ dk) {
+  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;   // 4 values of dk
+  const size_t total = (size_t)n * kKlDi;
+  if (e >= total) return;
+  float4 a = *reinterpret_cast<const float4*>(cpart + e);
+#pragma unroll
+  for (int g = 1; g < kKlHkv; ++g) {
+    const float4 x = *reinterpret_cast<const float4*>(cpart + (size_t)g * total + e);
     a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
   }
-  const int key = (kt << 5) + e / kKlDi;
-  if (key >= n) return;
-  float4* dst = reinterpret_cast<float4*>(dk + (size_t)key * kKlDi + e % kKlDi);
-  dst[0] = make_float4(a.x * grad_scale, a.y * grad_scale, a.z * grad_scale, a.w * grad_scale);
-  dst[1] = make_float4(b.x * grad_scale, b.y * grad_scale, b.z * grad_scale, b.w * grad_scale);
+  *reinterpret_cast<float4*>(dk + e) =
+      make_float4(a.x * grad_scale, a.y * grad_scale, a.z * grad_scale, a.w * grad_scale);
 }
 
 // loss = (1/n) sum_i kl_row[i], summed in a fixed order by one workgroup.
@@ -436,10 +599,7 @@ bool kl_shape_supported(const LayerShape& s, int d_idx) {
   return s.dtype == kBF16 && s.d == kKlD && s.hkv == kKlHkv && s.hq == kKlHq && d_idx == kKlDi;
 }
 
-size_t kl_partial_bytes(int n) {
-  const size_t nt = (size_t)(n + 31) / 32;
-  return nt * (nt + 1) / 2 * 32 * kKlDi * sizeof(float);
-}
+size_t kl_partial_bytes(int n) { return (size_t)kKlHkv * (size_t)n * kKlDi * sizeof(float); }
 
 hipError_t launch_kl_distill(const LayerShape& s, int d_idx, float idx_scale, const void* q,
                              const void* k, const void* q_idx, const void* k_idx,
@@ -451,14 +611,23 @@ hipError_t launch_kl_distill(const LayerShape& s, int d_idx, float idx_scale, co
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kl_tile_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kKlLds);
   if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kl_dk_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kl_tile_kernel, dim3(ntiles), dim3(512), kKlLds, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_idx), lse,
-                     lse_t, s.n, s.scale * kLog2e, idx_scale * kLog2e, kl_row, dq, dk_part,
-                     grad_scale);
+                     lse_t, s.n, s.scale * kLog2e, idx_scale * kLog2e, kl_row, dq, grad_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(kl_dk_reduce_kernel, dim3(ntiles), dim3(256), 0, stream, dk_part, s.n,
-                     grad_scale, dk);
+  const int kblocks = (ntiles + kDkWaves - 1) / kDkWaves;
+  hipLaunchKernelGGL(kl_dk_kernel, dim3(kblocks * kKlHkv), dim3(512), kDkLds, stream,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_idx), lse,
+                     lse_t, s.n, s.scale * kLog2e, idx_scale * kLog2e, dk_part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t quads = ((size_t)s.n * kKlDi + 3) / 4;
+  hipLaunchKernelGGL(kl_dk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream,
+                     dk_part, s.n, grad_scale, dk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (loss) {
     hipLaunchKernelGGL(kl_loss_kernel, dim3(1), dim3(256), 0, stream, kl_row, s.n, loss);

@@ -257,8 +257,13 @@ def test_kl_distill_validation(lib):
     assert lib.amtk_kl_workspace(ctypes.byref(b), 32, ctypes.byref(need)) == -2
     assert lib.amtk_kl_workspace(ctypes.byref(b), 0, ctypes.byref(need)) == -1
     assert lib.amtk_kl_workspace(ctypes.byref(b), 64, ctypes.byref(need)) == 0
-    nt = (1000 + 31) // 32
-    assert need.value >= nt * (nt + 1) // 2 * 32 * 64 * 4 + 32 * 1000 * 4
+    # dense LSE, student LSE and the key gradient's 8 per-KV-group shares:
+    # linear in n (no n x n-sized array)
+    assert 1000 * (32 + 1 + 8 * 64) * 4 <= need.value <= 1000 * (32 + 1 + 8 * 64) * 4 + 4096
+    big = _abi.AttnDesc(100000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    need_big = ctypes.c_size_t(0)
+    assert lib.amtk_kl_workspace(ctypes.byref(big), 64, ctypes.byref(need_big)) == 0
+    assert need_big.value <= 100000 * (32 + 1 + 8 * 64) * 4 + 4096     # 218 MB at 100K
     f = lib.kl_distill
     args = [FAKE] * 8
     assert f(ctypes.byref(b), 64, 0.0, *args, FAKE, need.value - 1, None) == -3

@@ -12,7 +12,10 @@ Small shapes are compared in full; the 4K and 32K indexer layers on seeded
 rows (KL, dq), on their last keys (dk: those need only the last rows), and
 through properties that hold at any size: sum_i <q_i, dq_i> = sum_j <k_j,
 dk_j>, sum_j dk_j = 0 (the loss ignores a shift of every k_idx row), and
-the loss as the mean of the rows.
+the loss as the mean of the rows. The query-major pass forms dS = Q - P per
+pair for KL and dq; the key gradient is built per KV group (each group's
+share of the head sum), so dq and dk round dS differently and the
+identities hold within bounds derived from the same per-pair bar.
 """
 import math
 
@@ -80,14 +83,27 @@ def _check_keys(kd, keys, dk, qi):
         assert np.all(err <= tol), f"key {j}: dk err {err.max()} (tol {tol.min()})"
 
 
-def _check_properties(kl, loss, dq, dk, qi, ki):
+def _check_properties(kl, loss, dq, dk, qi, ki, tau):
+    """Identities of the exact gradients. dq and dk are computed from two
+    roundings of dS = Q - P (the query-major pass forms Q - P per pair; the
+    key gradient adds the KV groups' shares of P separately), each within
+    eps (P_ij + Q_ij) of the exact dS with eps = 1e-4, the same bar as the
+    element-wise checks. Summed over all pairs, with sum_j (P_ij + Q_ij) = 2
+    per row:
+      |sum_i <q_i, dq_i> - sum_j <k_j, dk_j>| <= 4 eps tau max|q_i| max|k_j|,
+      |sum_j dk_j[d]| <= 2 eps (tau/N) sum_i |q_i[d]|."""
+    n = qi.shape[0]
+    eps = 1e-4
+    q64, k64 = qi.astype(np.float64), ki.astype(np.float64)
     assert abs(loss - float(np.mean(kl.astype(np.float64)))) <= 1e-6 * max(1.0, abs(loss))
-    lhs = float(np.sum(qi.astype(np.float64) * dq))
-    rhs = float(np.sum(ki.astype(np.float64) * dk))
-    scale = float(np.sum(np.abs(qi.astype(np.float64) * dq))) + 1e-30
-    assert abs(lhs - rhs) <= 1e-3 * scale, (lhs, rhs)
+    lhs = float(np.sum(q64 * dq))
+    rhs = float(np.sum(k64 * dk))
+    qn = float(np.max(np.linalg.norm(q64, axis=1)))
+    kn = float(np.max(np.linalg.norm(k64, axis=1)))
+    assert abs(lhs - rhs) <= 4 * eps * tau * qn * kn, (lhs, rhs)
     tot = dk.astype(np.float64).sum(axis=0)
-    assert np.all(np.abs(tot) <= 1e-3 * np.abs(dk).sum(axis=0) + 1e-12), tot
+    bound = 2 * eps * tau / n * np.abs(q64).sum(axis=0)
+    assert np.all(np.abs(tot) <= bound), (tot, bound)
 
 
 @pytest.mark.parametrize("n", [1, 32, 100, 161])
@@ -100,7 +116,7 @@ def test_kl_distill_small_shapes_every_row_and_key(gpu_lib, n):
     _check_keys(kd, list(range(n)), dk, qi)
     full = kd.full()
     assert abs(loss - full["loss"]) <= 1e-4 * max(1.0, abs(full["loss"]))
-    _check_properties(kl, loss, dq, dk, qi, ki)
+    _check_properties(kl, loss, dq, dk, qi, ki, kd.scale)
 
 
 def test_kl_distill_student_equals_teacher_gives_zero(gpu_lib):
@@ -151,4 +167,4 @@ def test_kl_distill_indexer_workload(gpu_lib, n):
     rows = sample_rows(w, n=n)[:: (8 if n == 4096 else 32)]
     _check_rows(kd, rows, kl, dq, qi, ki)
     _check_keys(kd, list(range(n - 40, n, 3)), dk, qi)
-    _check_properties(kl, loss, dq, dk, qi, ki)
+    _check_properties(kl, loss, dq, dk, qi, ki, kd.scale)
