@@ -104,7 +104,9 @@ def l2_read_ceiling(regions_mb=(1, 2, 3), mode=0, grid=2048, pass_bytes=8e9, rep
     of its own that fits its 4 MB L2 (calib/l2_read.hip), timed with HIP events
     on the launch stream; the best median over the region sizes. mode 0 streams
     contiguous 16-byte loads, mode 1 reads 256-byte rows at scattered positions
-    (the gather's access shape). Returns (GB/s, {region MB: GB/s})."""
+    (the gather's access shape) into registers, mode 2 the same rows into LDS
+    by direct global->LDS loads, 16 KiB per 64-lane workgroup (the gather's
+    own staging). Returns (GB/s, {region MB: GB/s})."""
     import ctypes
     import numpy as np
     import torch
@@ -125,8 +127,12 @@ def l2_read_ceiling(regions_mb=(1, 2, 3), mode=0, grid=2048, pass_bytes=8e9, rep
         if mode == 0:
             iters = max(1, int(pass_bytes / (8 * region)))
             nbytes = iters * 8 * region
-        else:
+        elif mode == 1:
             per_iter = grid * 16 * 64 * 256          # 64 rows per 16-lane group
+            iters = max(1, int(pass_bytes / per_iter))
+            nbytes = iters * per_iter
+        else:
+            per_iter = grid * 16384                  # 64-lane workgroups, 16 KiB rounds
             iters = max(1, int(pass_bytes / per_iter))
             nbytes = iters * per_iter
         times = []
@@ -422,9 +428,12 @@ def main():
     if args.calibrate_l2:
         best, per = l2_read_ceiling(mode=0)
         best_rows, per_rows = l2_read_ceiling(mode=1)
+        best_lds, per_lds = l2_read_ceiling(mode=2, grid=2560)
         print(json.dumps({"calibration": "L2 read, every XCD re-reading its own region",
                           "stream_GBs": best, "stream_by_region_MB": per,
-                          "rows_256B_GBs": best_rows, "rows_by_region_MB": per_rows}), flush=True)
+                          "rows_256B_GBs": best_rows, "rows_by_region_MB": per_rows,
+                          "rows_256B_to_lds_GBs": best_lds, "rows_to_lds_by_region_MB": per_lds}),
+              flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); the "

@@ -10,7 +10,9 @@
 //   mode 0: contiguous 16-byte loads, 256 threads walking the region in
 //           strides (the plain streaming ceiling);
 //   mode 1: 256-byte rows at pseudo-random row positions of the region, one
-//           row per 16 lanes (the access shape of a row gather).
+//           row per 16 lanes (the access shape of a row gather);
+//   mode 2: the rows of mode 1 brought into LDS by direct global->LDS loads,
+//           as the gather stages them (kernel below).
 // Nothing is written unless the XOR of everything read hits a fixed 128-bit
 // value, which keeps the loads alive without adding write traffic.
 #include <hip/hip_runtime.h>
@@ -83,6 +85,39 @@ __global__ __launch_bounds__(kThreads) void l2_rows_kernel(const uint4* __restri
     sink[blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// mode 2: the same 256-byte rows as mode 1, but brought into LDS with
+// global_load_lds_dwordx4 (16 bytes per lane, 4 rows per instruction), the
+// way the gather stages its keys and values: one 64-lane workgroup with a
+// 16 KiB LDS buffer (32 rows of keys and of values), 16 loads per round, all
+// of a round in flight before it is waited for; a lane then reads one word
+// of the buffer back so the loads cannot be elided.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__global__ __launch_bounds__(64) void l2_rows_lds_kernel(const uint4* __restrict__ buf,
+                                                        long region, int iters,
+                                                        uint4* __restrict__ sink) {
+  __shared__ __align__(256) unsigned char smem[16384];
+  const int xcd = blockIdx.x % kXcds;
+  const unsigned local = blockIdx.x / kXcds;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(buf + (long)xcd * region);
+  const unsigned rows = (unsigned)(region / 16);
+  const int lane = threadIdx.x;
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+  unsigned acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const unsigned t = (local * 64u + (unsigned)(4 * c + (lane >> 4))) + (unsigned)it * 7919u;
+      const unsigned row = (t * 2654435761u) % rows;
+      const unsigned char* src = base + (size_t)row * 256 + 16 * (lane & 15);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(lds + 1024u * c), 16, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    acc ^= *reinterpret_cast<const volatile unsigned*>(smem + 4 * lane + 256 * (it & 63));
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x * 64 + lane] = make_uint4(acc, 0, 0, 0);
+}
+
 }  // namespace
 
 extern "C" __attribute__((visibility("default")))
@@ -93,15 +128,18 @@ extern "C" __attribute__((visibility("default")))
  * practically impossible case above). Returns 0, -1 on bad arguments, or the
  * hipError_t of the launch. Bytes read per pass: mode 0: iters * 8 *
  * region_bytes; mode 1: iters * grid * 16 * 64 * 256 (64 rows of 256 bytes per
- * 16-lane group and pass). */
+ * 16-lane group and pass); mode 2 (64-lane workgroups): iters * grid * 16384. */
 int amtk_calib_l2_read(const void* buf, size_t region_bytes, int iters, int grid, int mode,
                        void* sink, void* stream) {
   if (!buf || !sink || region_bytes == 0 || region_bytes % 4096 || iters < 1 || grid < kXcds ||
-      grid % kXcds || (mode != 0 && mode != 1))
+      grid % kXcds || mode < 0 || mode > 2)
     return -1;
   const long region = (long)(region_bytes / sizeof(uint4));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (mode == 0)
+  if (mode == 2)
+    l2_rows_lds_kernel<<<grid, 64, 0, st>>>(static_cast<const uint4*>(buf), region, iters,
+                                            static_cast<uint4*>(sink));
+  else if (mode == 0)
     l2_stream_kernel<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(buf), region, iters,
                                                  static_cast<uint4*>(sink));
   else
