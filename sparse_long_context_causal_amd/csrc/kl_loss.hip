@@ -363,6 +363,21 @@ constexpr unsigned kDkLseT = kDkLse + 512;           // student LSE x log2e [32]
 constexpr unsigned kDkBuf = 40960;                   // one query tile's buffer
 constexpr unsigned kDkLds = 2 * kDkBuf;
 
+// The 16 floats at a, a + 32, a + 64, a + 96 (four runs of 4; byte address
+// a in LDS), in the order of a lane's score registers (query acc_row(r)),
+// read in one asm block that waits for them.
+__device__ __forceinline__ void lds_floats16(uint32_t a, float (&f)[16]) {
+  uint4 x[4];
+  lds_read4(a, a + 32, a + 64, a + 96, x[0], x[1], x[2], x[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[4 * j] = __uint_as_float(x[j].x);
+    f[4 * j + 1] = __uint_as_float(x[j].y);
+    f[4 * j + 2] = __uint_as_float(x[j].z);
+    f[4 * j + 3] = __uint_as_float(x[j].w);
+  }
+}
+
 // One 1 KiB piece (instruction c: rows 4c .. 4c+3) of a 32-row x 256-byte
 // tile of head `head` of X [n][heads][128] (rows r0 ..), laid out as the key
 // tiles of KLane: chunk j of row R at 16-byte position R*16 + (j ^ (R & 15)).
@@ -432,14 +447,14 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
       const int row = min(q0 + (int)drow, n - 1);
       const unsigned char* src = reinterpret_cast<const unsigned char*>(QI) + (size_t)row * (kKlDi * 2) + dpiece;
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + kDkQidx + 1024u * wave), 16, 0, 0);
-    } else if (wave == 4) {
-      // lane l: heads (l >> 5) and 2 + (l >> 5), query q0 + l % 32
-      const int row = min(q0 + col, n - 1);
-      lse_reg[0] = lse[(size_t)(g * kKlG + hf) * n + row];
-      lse_reg[1] = lse[(size_t)(g * kKlG + 2 + hf) * n + row];
-    } else if (wave == 5) {
-      lse_reg[0] = lse_t[min(q0 + col, n - 1)];
     }
+    // every wave loads (only waves 4 and 5 publish): no branch merges the
+    // loaded registers, which would make the compiler wait for all memory
+    // (the DMA just issued included). Wave 4, lane l: heads (l >> 5) and
+    // 2 + (l >> 5), query q0 + l % 32; wave 5: the student LSE.
+    const int row = min(q0 + col, n - 1);
+    lse_reg[0] = wave == 5 ? lse_t[row] : lse[(size_t)(g * kKlG + hf) * n + row];
+    lse_reg[1] = lse[(size_t)(g * kKlG + 2 + hf) * n + row];
   };
   auto publish_regs = [&](int qt) {   // after this wave's loads of tile qt landed
     float* buf = reinterpret_cast<float*>(smem + kDkBuf * (unsigned)(qt & 1));
@@ -469,7 +484,9 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
 
   issue_tile(qfirst);
   for (int qt = qfirst; qt < ntiles; ++qt) {
-    wait_vmem_all();                 // this wave's pieces and register loads of tile qt
+    // this wave's pieces and register loads of tile qt (the builtin, whose
+    // wait the compiler accounts for)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     publish_regs(qt);
     barrier_lds();                   // tile qt complete; tile qt-1 no longer read
     if (qt + 1 < ntiles) issue_tile(qt + 1);
@@ -486,12 +503,10 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
       ql.read(buf + kDkQ + 8192u * h, qc);
       f32x16 a;
       score_tile<bf16_t, kKlNc>(a, qc, kc);   // S[query][key]: lane = key, r = query
+      // (as asm reads that wait for LDS only: the compiler would otherwise
+      // wait for the next query tile's DMA before reading this buffer)
       float bias[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 b4 = *reinterpret_cast<const float4*>(lsel + 32 * h + 8 * j + 4 * hf);
-        bias[4 * j] = b4.x; bias[4 * j + 1] = b4.y; bias[4 * j + 2] = b4.z; bias[4 * j + 3] = b4.w;
-      }
+      lds_floats16(lds_addr(lsel + 32 * h + 4 * hf), bias);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(fmaf(a[r], c, -bias[r]));
@@ -513,13 +528,10 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
         t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf),
                                                     __builtin_bit_cast(bf16x8, kif[s]), t, 0, 0, 0);
       }
+      float bt[16];
+      lds_floats16(lds_addr(lsetl + 4 * hf), bt);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 b4 = *reinterpret_cast<const float4*>(lsetl + 8 * j + 4 * hf);
-        const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[4 * j + u] += fast_exp2(fmaf(t[4 * j + u], ct, -bt[u]));
-      }
+      for (int r = 0; r < 16; ++r) v[r] += fast_exp2(fmaf(t[r], ct, -bt[r]));
     }
     u32x4 bh[2], bl[2];
 #pragma unroll
