@@ -532,7 +532,9 @@ def main():
     # bytes are set against the measured L2 read ceiling; the bytes that came
     # from beyond L2 (FETCH_SIZE counters) are reported beside them.
     l2_gbs, _ = l2_read_ceiling()
-    log(f"[bench] L2 read ceiling (measured): {l2_gbs:.0f} GB/s")
+    stage_gbs, _ = l2_read_ceiling(mode=2, grid=2560)
+    log(f"[bench] L2 read ceiling (measured): {l2_gbs:.0f} GB/s; 256-byte rows into LDS by "
+        f"direct loads: {stage_gbs:.0f} GB/s")
     kernels[attn_name] = {"bound": "l2", "work": attn_bytes, "ms": per["sparse_attn"]}
     dom = max((kn for kn in kernels if kernels[kn]["work"]), key=lambda kn: kernels[kn]["ms"])
     kd = kernels[dom]
@@ -556,6 +558,10 @@ def main():
                 ent["GB/s"] = round(kv["work"] / (kv["ms"] * 1e-3) / 1e9, 1)
                 ent["frac_l2"] = round(ent["GB/s"] / l2_gbs, 4)
                 ent["l2_ceiling_GB/s"] = round(l2_gbs, 1)
+                # the gather stages its rows in LDS by direct global->LDS
+                # loads; that path's own measured ceiling
+                ent["lds_staging_ceiling_GB/s"] = round(stage_gbs, 1)
+                ent["frac_lds_staging"] = round(ent["GB/s"] / stage_gbs, 4)
                 beyond = traffic_for(kn, tkey) if kn in KERNEL_SOURCES else None
                 ent["beyond_l2_bytes"] = beyond
                 if beyond:
