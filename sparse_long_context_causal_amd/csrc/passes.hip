@@ -167,8 +167,12 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
   // busy together (left alone, the compiler issues the MFMAs in bursts that
   // stall the wave). The order is held by empty volatile asm statements
   // (which keep their program order): each one makes the next MFMA's key
-  // operand and the next group's inputs depend on the previous group's sums.
-  // The sums are formed in the same order as in stats(), so results match.
+  // operand and the next group's exponent arguments depend on the previous
+  // group's sums. The statements tie the fma results, which are fresh
+  // values, rather than elements of the score vector, which the compiler
+  // would first copy out (one v_mov per element: tying the scores cost 5 %
+  // of the pass). The sums are formed in the same order as in stats(), so
+  // results match.
   constexpr bool kInterleave = std::is_same<T, bf16_t>::value && (G % 2 == 0);
   constexpr int kEpg = 16 / NC;   // elements of the current head per MFMA
   auto step = [&](f32x16& nxt, uint4 (&kk)[NC], const uint4 (&qq)[NC], const f32x16& cur,
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
     for (int cc = 0; cc < NC; ++cc) {
       float x[kEpg];
 #pragma unroll
-      for (int e = 0; e < kEpg; ++e) x[e] = cur[cc * kEpg + e];
+      for (int e = 0; e < kEpg; ++e) x[e] = fmaf(cur[cc * kEpg + e], c, -mc);
       u32x4 kv = __builtin_bit_cast(u32x4, kk[cc]);
       if constexpr (kEpg == 2)
         asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]) : "v"(s0), "v"(s1));
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(512) void pass1_lse_kernel(const T* __restrict__ Q,
 #pragma unroll
       for (int e = 0; e < kEpg; ++e) {
         const int r = cc * kEpg + e;
-        const float y = fast_exp2(fmaf(x[e], c, -mc));
+        const float y = fast_exp2(x[e]);
         if (r & 1) s1 += y;
         else s0 += y;
       }
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     for (int cc = 0; cc < NC; ++cc) {
       float x[kEpg];
 #pragma unroll
-      for (int e = 0; e < kEpg; ++e) x[e] = cur[cc * kEpg + e];
+      for (int e = 0; e < kEpg; ++e) x[e] = fmaf(cur[cc * kEpg + e], c, -bias[h]);
       u32x4 kv = __builtin_bit_cast(u32x4, kc[cc]);
       if constexpr (kEpg == 2)
         asm volatile("" : "+v"(kv), "+v"(x[0]), "+v"(x[1]) : "v"(last));
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
 #pragma unroll
       for (int e = 0; e < kEpg; ++e) {
         const int r = cc * kEpg + e;
-        const float ev = fast_exp2(fmaf(x[e], c, -bias[h]));
+        const float ev = fast_exp2(x[e]);
         pacc[r] = h == 0 ? ev : pacc[r] + ev;
       }
       last = pacc[cc * kEpg + kEpg - 1];
