@@ -151,6 +151,45 @@ def l2_read_ceiling(regions_mb=(1, 2, 3), mode=0, grid=2048, pass_bytes=8e9, rep
     return max(res.values()), res
 
 
+def pass_mix_ceiling(iters=3000, reps=3):
+    """Measured compute ceilings of the passes' inner loop (calib/mix_ceiling.hip),
+    in TFLOP/s of bf16 MFMA work, random operands, one 512-thread workgroup per CU
+    (two waves per SIMD, the passes' occupancy): mode 0 the MFMA chains alone
+    (the rate the chip sustains under its power limit), mode 1 the same chains
+    with each head's fma/exp2/add per logit beside the next head's chain, in the
+    pass kernels' order. Timed with HIP events on the launch stream, median of
+    reps after one warm-up launch. Returns {"mfma_sustained": ..., "pass_mix": ...}."""
+    import ctypes
+    import numpy as np
+    import torch
+    if not os.path.exists(CALIB_LIB):
+        raise RuntimeError(f"{CALIB_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(CALIB_LIB)
+    fn = lib.amtk_calib_mix
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.empty(grid * 512, dtype=torch.float32, device=dev)
+    flops = float(grid) * 8 * iters * 64 * 32768   # 8 waves, 8 heads x 8 MFMAs per round
+    out = {}
+    for mode, name in ((0, "mfma_sustained"), (1, "pass_mix")):
+        times = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = fn(mode, iters, grid, sink.data_ptr(), stream.cuda_stream)
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"amtk_calib_mix returned {rc}")
+            torch.cuda.synchronize(dev)
+            if r:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        out[name] = flops / float(np.median(times)) / 1e12
+    return out
+
+
 def _host_cpu():
     """(cores this process may run on, CPU model name)."""
     cores = len(os.sched_getaffinity(0))
@@ -410,6 +449,9 @@ def main():
     ap.add_argument("--calibrate-l2", action="store_true",
                     help="only measure the L2 read ceiling (streaming and 256-byte rows, "
                          "1-3 MB per XCD) and exit")
+    ap.add_argument("--calibrate-mix", action="store_true",
+                    help="only measure the passes' compute ceilings (MFMA chains alone, and "
+                         "with the per-logit exp/sum work beside them) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run one plain device copy of MB megabytes (to scale HBM "
                          "traffic counters) and exit")
@@ -424,6 +466,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": nbytes,
                           "bytes_written": nbytes}), flush=True)
+        return
+    if args.calibrate_mix:
+        print(json.dumps({"calibration": "pass inner loop from registers, random bf16 operands",
+                          **{k + "_TFLOP/s": v for k, v in pass_mix_ceiling().items()}}),
+              flush=True)
         return
     if args.calibrate_l2:
         best, per = l2_read_ceiling(mode=0)
@@ -536,6 +583,13 @@ def main():
     log(f"[bench] L2 read ceiling (measured): {l2_gbs:.0f} GB/s; 256-byte rows into LDS by "
         f"direct loads: {stage_gbs:.0f} GB/s")
     kernels[attn_name] = {"bound": "l2", "work": attn_bytes, "ms": per["sparse_attn"]}
+    # The passes are bound by MFMA and VALU work together at the clock the
+    # chip sustains under that load: their rates are also set against the
+    # measured rate of their own inner loop run from registers (bf16 only).
+    mix = pass_mix_ceiling() if w.dtype == "bf16" else None
+    if mix:
+        log(f"[bench] pass inner loop ceilings (measured): MFMA chains alone "
+            f"{mix['mfma_sustained']:.0f} TFLOP/s, with the exp/sum work {mix['pass_mix']:.0f} TFLOP/s")
     dom = max((kn for kn in kernels if kernels[kn]["work"]), key=lambda kn: kernels[kn]["ms"])
     kd = kernels[dom]
     tkey = w.name if qb == 1 else f"{w.name}_qb{qb}"
@@ -571,6 +625,10 @@ def main():
             else:
                 ent["TFLOP/s"] = round(kv["work"] / (kv["ms"] * 1e-3) / 1e12, 1)
                 ent["frac_mfma"] = round(ent["TFLOP/s"] / peak_mfma, 4)
+                if mix and kn in ("pass1_lse", "pass2_filter", "pass2_colsum"):
+                    ent["mfma_sustained_TFLOP/s"] = round(mix["mfma_sustained"], 1)
+                    ent["pass_mix_ceiling_TFLOP/s"] = round(mix["pass_mix"], 1)
+                    ent["frac_pass_mix_ceiling"] = round(ent["TFLOP/s"] / mix["pass_mix"], 4)
         summary[kn] = ent
     if not w.indexer_d:
         t12 = (per["pass1_lse"] + per[names[1]]) * 1e-3

@@ -288,3 +288,23 @@ def test_binding_fails_loudly_without_library(tmp_path):
     from sparse_long_context_causal_amd import _abi
     with pytest.raises(RuntimeError):
         _abi.open_library(str(tmp_path / "missing.so"))
+
+
+def test_calibration_library_exports_its_two_kernels():
+    """bench.py's measured ceilings come from libamtk_calib.so: the L2 read
+    calibration and the passes' inner-loop compute ceiling."""
+    from sparse_long_context_causal_amd import build
+    if not os.path.exists(build.CALIB_LIB):
+        build.build(verbose=False)
+    out = subprocess.run(["nm", "-D", "--defined-only", build.CALIB_LIB], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert {"amtk_calib_l2_read", "amtk_calib_mix"} <= exported
+    cal = ctypes.CDLL(build.CALIB_LIB)
+    cal.amtk_calib_mix.restype = ctypes.c_int
+    cal.amtk_calib_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    # rejected on the host before any HIP call
+    assert cal.amtk_calib_mix(2, 1, 1, ctypes.c_void_p(16), None) != 0
+    assert cal.amtk_calib_mix(0, 0, 1, ctypes.c_void_p(16), None) != 0
+    assert cal.amtk_calib_mix(0, 1, 1, None, None) != 0
