@@ -410,29 +410,31 @@ __device__ __forceinline__ void raise_bound(RowState& rs, const unsigned* words,
   rs.btau[r] = bt;
 }
 
-// The same on row state held in registers (cnt = candidates appended so
-// far; seen, cge and bt as last left): every lane serving the row runs it,
-// so all of them keep the same state. The histogram words of the next 8
-// bins come in one batch of reads, as the bound rarely moves further.
-__device__ __forceinline__ void raise_bound_regs(const unsigned* words, int budget, int cnt,
-                                                 int& seen, int& cge, int& bt) {
-  int cg = cge + (cnt - seen);
+// The same on row state held in registers (cge = candidates in bins >= bt
+// after cg, the count including this tile's appends; hb = the count of bin
+// bt itself): every lane serving the row runs it, so all of them keep the
+// same state. Called only when the bound must rise (cg - hb >= budget). The
+// histogram words of the next 8 bins come in one batch of reads, as the
+// bound rarely moves further; on return hb holds the count of the new bin.
+__device__ __forceinline__ void raise_bound_regs(const unsigned* words, int budget, int cg,
+                                                 int& cge, int& bt, int& hb_bt) {
   const int w0 = bt >> 1;
   unsigned wv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) wv[j] = words[min(w0 + j, kFBinWords - 1)];
   int b = bt;
-  while (b < kFBins - 1) {
+  int hb = 0;
+  while (true) {
     const int j = (b >> 1) - w0;
     const unsigned w = j == 0 ? wv[0] : j == 1 ? wv[1] : j == 2 ? wv[2] : j == 3 ? wv[3] : words[b >> 1];
-    const int hb = (int)((w >> ((b & 1) * 16)) & 0xffffu);
-    if (cg - hb < budget) break;
+    hb = (int)((w >> ((b & 1) * 16)) & 0xffffu);
+    if (b >= kFBins - 1 || cg - hb < budget) break;
     cg -= hb;
     ++b;
   }
-  seen = cnt;
   cge = cg;
   bt = b;
+  hb_bt = hb;
 }
 
 // Partial-mass layout: element (register r, source lane) of KV head g's
@@ -601,8 +603,10 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   };
   float blk = 0.f;   // KB > 1: this query's mass over the current key block (this wave's heads)
   // KB = 1: the filter state of the row this lane serves, kept in registers
-  // (the same in every lane of the row's group; written to rs at the end)
-  int r_cnt = 0, r_seen = 0, r_cge = 0, r_bt = 0;
+  // (the same in every lane of the row's group; written to rs at the end):
+  // candidates appended, candidates in bins >= the bound bin, the bound bin
+  // and the count of that bin itself
+  int r_cnt = 0, r_cge = 0, r_bt = 0, r_hb = 0;
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
@@ -713,6 +717,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
           pm[e] = p * inv_hq;
         }
       }
+      int in_bt = 0;   // this tile's appends that fall in the bound's own bin
       for (int e = 0; e < epl; ++e) {
         const int mo = e * lpq + own_j;
         float p;
@@ -722,21 +727,28 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         const int key = k0 + mo;
         const bool flag = own_ok && bits >= thr && (!diag || key <= own_q);
         const unsigned long long m = __ballot(flag) & grp_mask;
+        const int bin = filter_bin(p);
         if (flag) {
           const int at = pos + __popcll(m & below);
           if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(bits, (unsigned)key);
-          if (live) {
-            const int bin = filter_bin(p);
-            lds_add(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
-          }
+          if (live) lds_add(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
         }
+        in_bt += __popcll(__ballot(flag && bin == r_bt) & grp_mask);
         pos += __popcll(m);
       }
-      // the bound can only rise after appends (the histogram is unchanged
-      // otherwise)
-      if (pos != pos0) {   // (uniform over the row's group; never for rows past n)
+      // The bound can only rise after appends (the histogram is unchanged
+      // otherwise), and only when more than k candidates lie above its own
+      // bin; both counts are kept in registers, so the histogram is read
+      // only when the bound moves. (uniform over the row's group; never for
+      // rows past n)
+      if (pos != pos0) {
+        const int cg = r_cge + (pos - pos0);
         r_cnt = pos;
-        if (pos <= cap) raise_bound_regs(own_hist, budget, pos, r_seen, r_cge, r_bt);
+        if (pos <= cap) {
+          r_hb += in_bt;
+          if (r_bt < kFBins - 1 && cg - r_hb >= budget) raise_bound_regs(own_hist, budget, cg, r_cge, r_bt, r_hb);
+          else r_cge = cg;
+        }
       }
     } else {
       // ---- key blocks of KB = 64 tokens = two key tiles
