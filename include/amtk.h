@@ -162,8 +162,8 @@ int amtk_sparse_attn_workspace(const amtk_attn_desc* attn, size_t* bytes);
  * lives in lse_sparse when given, else in ws). Rows whose ids are ascending
  * (as topk_support writes them) are split this way; a row whose ids are not
  * ascending is attended whole in the first window. Where the windowed form
- * does not apply (other shapes than bf16, d = 128, hkv = 8, hq = 32; n of
- * one window) the call is sparse_attn.
+ * does not apply (other shapes than bf16, d = 128, hq / hkv in {1, 2, 4, 8}
+ * with n * hkv * 256 < 2^32; n of one window) the call is sparse_attn.
  *
  * Arguments as sparse_attn, plus ws: device scratch of ws_bytes >=
  * amtk_sparse_attn_workspace bytes, 256-byte aligned, owned by the caller

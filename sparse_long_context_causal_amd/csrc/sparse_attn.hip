@@ -454,18 +454,40 @@ __device__ __forceinline__ float quad_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), R * 0x55, 0xF, 0xF, false));
 }
 
-template <bool kUnitTokens>   // true: key_block == 1; false: key_block % 16 == 0
+// G query heads per KV head (1, 2, 4 or 8): the query fragment's column n
+// holds head n % G, the weights' A-operand rows [0, G) carry hi and rows
+// [G, 2G) lo, so result row 4q + r belongs to head (4q + r) % G. Per-head
+// factors (rescale, normalisation, window merge) are the same in every lane
+// of a head, and lane h < G holds head h: they are read with readlane.
+template <int G>
+__device__ __forceinline__ void head_factors(float x, float (&f)[4]) {
+  float hv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    hv[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), h));
+  const bool odd = (threadIdx.x >> 4) & 1;   // lane group q odd
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (G == 8) f[r] = odd ? hv[4 + r] : hv[r];
+    else f[r] = hv[r % G];
+  }
+}
+
+template <bool kUnitTokens, int G>   // kUnitTokens true: key_block == 1; false: key_block % 16 == 0
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
-    float* __restrict__ lse_out, int n, int key_block, int max_units, float c,
+    float* __restrict__ lse_out, int n, int hkv_log2, int key_block, int max_units, float c,
     const int32_t* __restrict__ wstart, int nwin, int win) {
-  constexpr int D = 128, HKV = 8, G = 4, HQ = HKV * G;
-  constexpr unsigned kRowBytes = HKV * D * sizeof(bf16_t);   // one token, all KV heads
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per KV head");
+  constexpr int D = 128;
+  const int hkv = 1 << hkv_log2;   // a power of two: rows and heads by shifts
+  const int HQ = hkv * G;
+  const unsigned row_shift = (unsigned)hkv_log2 + 8u;   // bytes of one token, all KV heads: hkv * 256
   __shared__ __align__(256) unsigned char smem[2 * kTileBytes];   // keys, values of a chunk
   const int lane = threadIdx.x;
-  const int i = n - 1 - (int)(blockIdx.x / HKV);   // longest rows first
-  const int g = (int)(blockIdx.x % HKV);
+  const int i = n - 1 - (int)(blockIdx.x >> hkv_log2);   // longest rows first
+  const int g = (int)(blockIdx.x & (unsigned)(hkv - 1));
   const int m = lane & 15, q = lane >> 4;
   int cnt = min(max(count[i], 0), max_units);
   // Key windows (nwin > 0): this launch takes the support's units that lie
@@ -539,7 +561,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     for (int c8 = 0; c8 < 8; ++c8) {
       int r;
       const bool ok = token_row(t0, 4 * c8 + q, kUnitTokens ? raw[c8] : raw[4 * (c8 >> 2)], r);
-      off[c8] = (unsigned)(ok ? r : i) * kRowBytes + ((c8 & 1) ? xo1 : xo0);
+      off[c8] = ((unsigned)(ok ? r : i) << row_shift) + ((c8 & 1) ? xo1 : xo0);
     }
     int r;
     int own = raw[8];
@@ -559,10 +581,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     }
   };
 
-  // query fragment: B operand column n = head n%4, d 32s + 8q + [0, 8)
+  // query fragment: B operand column n = head n%G, d 32s + 8q + [0, 8)
   u32x4 qf[4];
   {
-    const bf16_t* qr = Q + ((size_t)i * HQ + G * g + (lane & 3)) * D + 8 * q;
+    const bf16_t* qr = Q + ((size_t)i * HQ + G * g + (lane & (G - 1))) * D + 8 * q;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qr + 32 * s);
   }
@@ -581,7 +603,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) va[blk] = vb0 ^ (32u * blk);
   }
-  const float lo_sel = (m >= 4 && m < 8) ? 1.0f : 0.0f;   // A-operand rows 4-7 carry lo
+  const float lo_sel = (m >= G && m < 2 * G) ? 1.0f : 0.0f;   // A-operand rows G..2G-1 carry lo
 
   int raw[9];
   unsigned off[8];
@@ -615,7 +637,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
         sc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[4 * sg + s]),
                                                          __builtin_bit_cast(bf16x8, qf[s]), sc[sg], 0, 0, 0);
     }
-    float x[8];   // index 4 sigma + r: token 16 sigma + 4q + r, head lane%4
+    float x[8];   // index 4 sigma + r: token 16 sigma + 4q + r, head lane%G
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3];
     if (valid != 0xffffffffu) {
@@ -632,14 +654,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     if (__ballot(mnew != mrun)) {   // a head's maximum moved: rescale
       const float alpha = mnew == mrun ? 1.0f : fast_exp2(mrun - mnew);
       lrun *= alpha;
-      const float a0 = quad_bcast<0>(alpha), a1 = quad_bcast<1>(alpha);
-      const float a2 = quad_bcast<2>(alpha), a3 = quad_bcast<3>(alpha);
+      float a[4];
+      head_factors<G>(alpha, a);
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
-        acc[bb][0] *= a0;
-        acc[bb][1] *= a1;
-        acc[bb][2] *= a2;
-        acc[bb][3] *= a3;
+        acc[bb][0] *= a[0];
+        acc[bb][1] *= a[1];
+        acc[bb][2] *= a[2];
+        acc[bb][3] *= a[3];
       }
       mrun = mnew;
     }
@@ -664,23 +686,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
                                                         __builtin_bit_cast(bf16x8, vv), acc[bb], 0, 0, 0);
     }
   }
-  float l = lrun + __shfl_xor(lrun, 16, 64);   // every lane: head lane%4
+  float l = lrun + __shfl_xor(lrun, 16, 64);   // every lane: head lane%G
   l += __shfl_xor(l, 32, 64);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const float i0 = quad_bcast<0>(inv), i1 = quad_bcast<1>(inv);
-  const float i2 = quad_bcast<2>(inv), i3 = quad_bcast<3>(inv);
-  // result row 4q + r: q = 0 hi, q = 1 lo of head r. Lanes of group 0
-  // write heads 0, 1 and lanes of group 1 heads 2, 3 (d = 16 blk + m).
-  const bool upper = q == 1;
-  float* orow = O + ((size_t)i * HQ + G * g + (upper ? 2 : 0)) * D + m;
-  // this window's LSE of head lane%4 (log2 units)
+  // this window's LSE of head lane%G (log2 units)
   const float lw = l > 0.f ? mrun + log2f(l) : -INFINITY;
   float lnew = lw;
+  const int rsel = (G == 4 ? q == 1 : G == 8 ? (q >> 1) == 1 : false) ? 2 : 0;
+  const int hbase = G == 8 ? 4 * (q & 1) + rsel : rsel;
+  const bool store = G == 8 ? true : G == 4 ? q < 2 : q == 0;
+  float* const obase = O + ((size_t)i * HQ + G * g + hbase) * D + m;
+  // merging: every earlier output value this lane rewrites, read in one batch
+  // (in flight together with the running LSE read below)
+  float prev[8][2];
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) prev[bb][0] = prev[bb][1] = 0.f;
+  if (merge && store) {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      prev[bb][0] = obase[16 * bb];
+      if constexpr (G > 1) prev[bb][1] = obase[D + 16 * bb];
+    }
+  }
+  // Output of this window, combined with the earlier windows' when merging:
+  // O = O_old * wa + O_win * wb per head (wa = 1 - wb = 0 without a merge),
+  // with L = logaddexp(L_old, L_win), wa = exp(L_old - L), wb = exp(L_win - L).
+  float wa = 0.f, wb = 1.f;
   if (merge) {
-    // O = O_old * exp(L_old - L) + O_win * exp(L_win - L), L = logaddexp
-    const float lold = lse_out[(size_t)(G * g + (lane & 3)) * n + i] * kLog2e;
+    const float lold = lse_out[(size_t)(G * g + (lane & (G - 1))) * n + i] * kLog2e;
     const float mx = fmaxf(lold, lw);
-    float wa = 1.f, wb = 0.f;
+    wa = 1.f;
+    wb = 0.f;
     lnew = lold;
     if (lw > -INFINITY) {
       const float ea = fast_exp2(lold - mx), eb = fast_exp2(lw - mx);
@@ -689,34 +725,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
       wa = ea / sum;
       wb = eb / sum;
     }
-    const float wa0 = quad_bcast<0>(wa), wa1 = quad_bcast<1>(wa);
-    const float wa2 = quad_bcast<2>(wa), wa3 = quad_bcast<3>(wa);
-    const float wb0 = quad_bcast<0>(wb) * i0, wb1 = quad_bcast<1>(wb) * i1;
-    const float wb2 = quad_bcast<2>(wb) * i2, wb3 = quad_bcast<3>(wb) * i3;
+  }
+  float fa[4], fb[4];   // per result row r of this lane: the head's wa and wb / l
+  head_factors<G>(wa, fa);
+  head_factors<G>(wb * inv, fb);
+  // Result row 4q + r is head (4q + r) % G: hi for rows below G, lo for rows
+  // G..2G-1 (higher rows are never used). A head's hi and lo rows meet in
+  // one lane for G <= 2, in lane groups q and q^1 for G = 4 (xor 16) and q
+  // and q^2 for G = 8 (xor 32). Then each storing lane group writes two
+  // heads at d = 16 blk + m: G = 4: group 0 heads 0-1, group 1 heads 2-3;
+  // G = 8: groups 0, 2, 1, 3 heads 0-1, 2-3, 4-5, 6-7.
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      f32x4 t = acc[bb];
+  for (int bb = 0; bb < 8; ++bb) {
+    f32x4 t = acc[bb];
+    float o0, o1;
+    if constexpr (G == 1) {
+      o0 = t[0] + t[1];
+      o1 = 0.f;
+    } else if constexpr (G == 2) {
+      o0 = t[0] + t[2];
+      o1 = t[1] + t[3];
+    } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], 16, 64);
-      if (q < 2) {
-        const float o0 = orow[16 * bb], o1 = orow[D + 16 * bb];
-        orow[16 * bb] = upper ? fmaf(o0, wa2, t[2] * wb2) : fmaf(o0, wa0, t[0] * wb0);
-        orow[D + 16 * bb] = upper ? fmaf(o1, wa3, t[3] * wb3) : fmaf(o1, wa1, t[1] * wb1);
-      }
+      for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], G == 4 ? 16 : 32, 64);
+      o0 = rsel ? t[2] : t[0];
+      o1 = rsel ? t[3] : t[1];
     }
-  } else {
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      f32x4 t = acc[bb];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], 16, 64);
-      if (q < 2) {
-        orow[16 * bb] = upper ? t[2] * i2 : t[0] * i0;
-        orow[D + 16 * bb] = upper ? t[3] * i3 : t[1] * i1;
-      }
+    if (store) {
+      const float fa0 = rsel ? fa[2] : fa[0], fa1 = rsel ? fa[3] : fa[1];
+      const float fb0 = rsel ? fb[2] : fb[0], fb1 = rsel ? fb[3] : fb[1];
+      float* orow = obase + 16 * bb;
+      orow[0] = merge ? fmaf(prev[bb][0], fa0, o0 * fb0) : o0 * fb0;
+      if constexpr (G > 1) orow[D] = merge ? fmaf(prev[bb][1], fa1, o1 * fb1) : o1 * fb1;
     }
   }
-  if (lse_out && lane < 4)
+  if (lse_out && lane < G)
     lse_out[(size_t)(G * g + lane) * n + i] = lnew > -INFINITY ? lnew * kLn2 : -INFINITY;
 }
 
@@ -769,7 +812,22 @@ static hipError_t run_attn(const LayerShape& s, int key_block, int max_units, co
 
 static int slice_width(const LayerShape& s) { return s.hkv * s.d / 64; }
 
+// The MFMA gather: bf16, d = 128, G = Hq/Hkv in {1, 2, 4, 8}, a power-of-two
+// number of KV heads as long as token rows of all KV heads stay within
+// 32-bit byte offsets; single tokens or key blocks of a multiple of 16
+// tokens.
+static bool mfma_attn_shape(const LayerShape& s, int key_block) {
+  if (s.dtype != kBF16 || s.d != 128 || s.hkv < 1 || s.hq % s.hkv) return false;
+  if (s.hkv & (s.hkv - 1)) return false;
+  const int G = s.hq / s.hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  if ((unsigned long long)s.n * (unsigned long long)s.hkv * 256ull > 0xFFFFFFFFull) return false;
+  return key_block == 1 || key_block % 16 == 0;
+}
+
 bool sparse_shape_supported(const LayerShape& s) {
+  // key_block is 1 or 64 at every entry point: both run on the MFMA gather
+  if (mfma_attn_shape(s, 1)) return true;
   if (s.hkv < 1 || s.hq % s.hkv) return false;
   const int G = s.hq / s.hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
@@ -809,17 +867,33 @@ static hipError_t attn_by_e(const LayerShape& s, int key_block, int max_units, c
   return hipErrorInvalidValue;
 }
 
+// One launch of the MFMA gather over rows >= n - rows (window w of nwin, or
+// the whole support when nwin = 0).
+static void launch_mfma_attn(const LayerShape& s, int key_block, int max_units, const void* q,
+                             const void* k, const void* v, const int32_t* idx,
+                             const int32_t* count, float* o, float* lse, long long rows,
+                             const int32_t* starts, int nwin, int w, hipStream_t stream) {
+  const int G = s.hq / s.hkv;
+  const bool unit = key_block == 1;
+  auto kern = G == 1 ? (unit ? sparse_attn_mfma_kernel<true, 1> : sparse_attn_mfma_kernel<false, 1>)
+            : G == 2 ? (unit ? sparse_attn_mfma_kernel<true, 2> : sparse_attn_mfma_kernel<false, 2>)
+            : G == 4 ? (unit ? sparse_attn_mfma_kernel<true, 4> : sparse_attn_mfma_kernel<false, 4>)
+                     : (unit ? sparse_attn_mfma_kernel<true, 8> : sparse_attn_mfma_kernel<false, 8>);
+  int hkv_log2 = 0;
+  while ((1 << hkv_log2) < s.hkv) ++hkv_log2;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rows * s.hkv)), dim3(64), 0, stream,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), idx, count, o, lse, s.n, hkv_log2, key_block,
+                     max_units, s.scale * kLog2e, starts, nwin, w);
+}
+
 hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units, const void* q,
                               const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream) {
-  if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32 &&
-      (key_block == 1 || key_block % 16 == 0)) {
-    auto kern = key_block == 1 ? sparse_attn_mfma_kernel<true> : sparse_attn_mfma_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)s.n * 8u), dim3(64), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, key_block,
-                       max_units, s.scale * kLog2e, nullptr, 0, 0);
+  if (mfma_attn_shape(s, key_block)) {
+    launch_mfma_attn(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, s.n, nullptr, 0,
+                     0, stream);
     return hipGetLastError();
   }
   if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32) {
@@ -849,8 +923,7 @@ constexpr int kWindowTokens = 8192;
 constexpr int kMaxWindows = 64;
 
 static bool windowed_shape(const LayerShape& s, int key_block) {
-  return s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32 &&
-         (key_block == 1 || key_block % 16 == 0);
+  return mfma_attn_shape(s, key_block);
 }
 
 static int window_tokens(const LayerShape& s) {
@@ -887,13 +960,10 @@ hipError_t launch_sparse_attn_windowed(const LayerShape& s, int key_block, int m
   hipLaunchKernelGGL(support_windows_kernel, dim3((unsigned)((s.n + 3) / 4)), dim3(256), 0, stream,
                      idx, count, s.n, max_units, key_block, wt, nwin, starts);
   hipError_t e = hipGetLastError();
-  auto kern = key_block == 1 ? sparse_attn_mfma_kernel<true> : sparse_attn_mfma_kernel<false>;
   for (int w = 0; w < nwin && e == hipSuccess; ++w) {
     const long long rows = (long long)s.n - (long long)w * wt;   // rows >= the window's first token
-    hipLaunchKernelGGL(kern, dim3((unsigned)rows * 8u), dim3(64), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), idx, count, o, lse_run, s.n, key_block,
-                       max_units, s.scale * kLog2e, starts, nwin, w);
+    launch_mfma_attn(s, key_block, max_units, q, k, v, idx, count, o, lse_run, rows, starts, nwin,
+                     w, stream);
     e = hipGetLastError();
   }
   return e;

@@ -60,6 +60,7 @@ def _full_check(amtk, x, dtype, k, key_block=1, rows=None, cap=0):
     (97, 16, 8, 128, "bf16", 9),    # G = 2
     (161, 8, 1, 64, "bf16", 11),    # G = 8, d = 64
     (90, 4, 2, 128, "f32", 6),      # fp32, d = 128
+    (110, 8, 4, 128, "bf16", 8),    # G = 2, four KV heads
 ])
 def test_small_shapes_all_rows(gpu_lib, n, hq, hkv, d, dtype, k):
     x = random_inputs(n, hq, hkv, d, dtype, seed=n * 7 + hq, sink=True)
@@ -258,17 +259,19 @@ def test_sparse_attn_one_token_and_empty(gpu_lib):
             np.testing.assert_array_equal(out[i, h], x["v"][i // 2, h // 4])
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (8, 1)])
 @pytest.mark.parametrize("key_block", [1, 64])
-def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block):
-    """The MFMA path (bf16, d=128, 32/8 heads) on hand-made supports: ids in
-    random order (the running maximum moves late), negative ids and ids past
-    the row mixed in, counts above max_units (clamped), empty rows. Every row
-    is checked against the oracle on the ids the contract keeps."""
+def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block, hq, hkv):
+    """The MFMA path (bf16, d=128; 1, 2, 4 or 8 query heads per KV head) on
+    hand-made supports: ids in random order (the running maximum moves late),
+    negative ids and ids past the row mixed in, counts above max_units
+    (clamped), empty rows. Every row is checked against the oracle on the ids
+    the contract keeps."""
     import torch
     amtk = gpu_lib
     n, max_units = 300, 48
     rng = np.random.default_rng(77 + key_block)
-    x = random_inputs(n, 32, 8, 128, "bf16", seed=43, sink=True)
+    x = random_inputs(n, hq, hkv, 128, "bf16", seed=43 + hq + hkv, sink=True)
     layer = OracleLayer(x["q"], x["k"], x["v"])
     idx = np.full((n, max_units), -1, dtype=np.int32)
     cnt = np.zeros(n, dtype=np.int32)

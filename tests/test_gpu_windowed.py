@@ -125,6 +125,28 @@ def test_windowed_key_block_supports(gpu_lib):
         assert float(np.max(np.abs(o2[i].astype(np.float64) - o_ref))) <= TOL_OUT["bf16"], f"row {i}"
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (4, 1), (16, 2)])
+def test_windowed_other_head_layouts(gpu_lib, hq, hkv):
+    """The windowed gather with 1, 2, 4 or 8 query heads per KV head and other
+    KV head counts: two windows (8192 + 1808 tokens), against the one-pass
+    gather and the oracle on rows on both sides of the window edge."""
+    n, k = 10000, 96
+    x = random_inputs(n, hq, hkv, 128, "bf16", seed=101 + hq + hkv, sink=True)
+    d = upload(x, "bf16")
+    idx, cnt = _token_supports(n, k, 102 + hq)
+    o1, l1, o2, l2 = _run_both(gpu_lib, d, idx, cnt, 1, True)
+    _compare(o1, l1, o2, l2)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    for i in (3, 8191, 8192, 9999):
+        toks = _row_tokens(idx, cnt, i, k)
+        if not toks:
+            assert np.all(o2[i] == 0)
+            continue
+        o_ref, l_ref = layer.attention_on(i, toks)
+        assert float(np.max(np.abs(o2[i].astype(np.float64) - o_ref))) <= TOL_OUT["bf16"], f"row {i}"
+        assert float(np.max(np.abs(l2[:, i] - l_ref))) <= TOL_LSE["bf16"], f"row {i} lse"
+
+
 def test_windowed_one_window_is_sparse_attn(gpu_lib):
     """n within one window: the call is the one-pass gather, bit for bit."""
     n, k = 3000, 40
