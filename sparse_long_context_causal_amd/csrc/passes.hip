@@ -23,9 +23,13 @@
 //   * pass 1 keeps an online max / sum per (head, query) in registers;
 //   * pass 2 turns logits into probabilities with pass 1's LSE, sums the G
 //     heads in registers, and the Hkv partial sums meet in LDS (double
-//     buffered, one barrier per key tile). Each wave then owns 32/Hkv query
-//     rows: it reduces their masses over the KV heads in a fixed order and
-//     filters them against the row's bound, so row state needs no atomics.
+//     buffered, one barrier per key tile). Row owners then reduce their
+//     rows' masses over the KV heads in a fixed order and filter them against
+//     the row's bound, so row state needs no atomics. With 8 KV heads only
+//     waves 0..3 own rows (8 each): waves 4..7, which share their SIMDs, go
+//     on to the next key tile's MFMAs while the owners filter (a partial
+//     buffer is rewritten two tiles later, after the next barrier); with
+//     other head counts every wave owns 32/Hkv rows.
 // Workgroups are issued longest-row first (causal load balance).
 //
 // Streaming filter (pass 2). Per query row, an LDS histogram over mass bins
@@ -473,6 +477,33 @@ __device__ __forceinline__ void read_partials_hk8(uint32_t a0, uint32_t a1, f32x
       : "memory");
 }
 
+// The same for four keys (addresses a[0..3]), one wait.
+__device__ __forceinline__ void read_partials_hk8x4(const uint32_t (&a)[4], f32x2 (&v)[16]) {
+  asm volatile(
+      "ds_read2st64_b32 %0, %16 offset1:17\n\t"
+      "ds_read2st64_b32 %1, %16 offset0:34 offset1:51\n\t"
+      "ds_read2st64_b32 %2, %16 offset0:68 offset1:85\n\t"
+      "ds_read2st64_b32 %3, %16 offset0:102 offset1:119\n\t"
+      "ds_read2st64_b32 %4, %17 offset1:17\n\t"
+      "ds_read2st64_b32 %5, %17 offset0:34 offset1:51\n\t"
+      "ds_read2st64_b32 %6, %17 offset0:68 offset1:85\n\t"
+      "ds_read2st64_b32 %7, %17 offset0:102 offset1:119\n\t"
+      "ds_read2st64_b32 %8, %18 offset1:17\n\t"
+      "ds_read2st64_b32 %9, %18 offset0:34 offset1:51\n\t"
+      "ds_read2st64_b32 %10, %18 offset0:68 offset1:85\n\t"
+      "ds_read2st64_b32 %11, %18 offset0:102 offset1:119\n\t"
+      "ds_read2st64_b32 %12, %19 offset1:17\n\t"
+      "ds_read2st64_b32 %13, %19 offset0:34 offset1:51\n\t"
+      "ds_read2st64_b32 %14, %19 offset0:68 offset1:85\n\t"
+      "ds_read2st64_b32 %15, %19 offset0:102 offset1:119\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+        "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
 // HK: the KV heads if fixed at 8, else 0. CS: instead of filtering each
 // row, write the column sums of the mass over the tile's rows (selection
 // blocks of consecutive queries share one support; KB = 1 only).
@@ -524,11 +555,16 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
 
   // Row ownership: wave w owns query rows [w*qpw, (w+1)*qpw) of the tile;
   // lpq lanes serve one row, each with epl of its 32 keys.
-  const int qpw = 32 / hkv, lpq = 2 * hkv, epl = 16 / hkv;
-  const int own_n = wave * qpw + lane / lpq;       // tile-local row this lane serves
+  // With the KV heads fixed at 8 only waves 0..3 own rows (8 each, 8 lanes a
+  // row, 4 keys a lane): waves 4..7, which share their SIMDs, run the next
+  // tile's MFMAs while the owners filter.
+  constexpr int kOwnerWaves = HK == 8 ? 4 : 0;
+  const bool owner_wave = HK == 8 ? wave < kOwnerWaves : true;
+  const int qpw = HK == 8 ? 8 : 32 / hkv, lpq = HK == 8 ? 8 : 2 * hkv, epl = HK == 8 ? 4 : 16 / hkv;
+  const int own_n = owner_wave ? wave * qpw + lane / lpq : 0;   // tile-local row this lane serves
   const int own_j = lane % lpq;
   const int own_q = q0 + own_n;
-  const bool own_ok = own_q < n;
+  const bool own_ok = owner_wave && own_q < n;
   const unsigned long long grp_mask =
       (lpq == 64 ? ~0ull : ((1ull << lpq) - 1ull)) << ((lane / lpq) * lpq);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -666,6 +702,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[wb + kPartPitch * r] = pacc[r];
       barrier_lds();   // partial masses visible
+      if (!owner_wave) continue;   // (uniform per wave)
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       // A mass passes the bound bin exactly when its bit pattern is at least
       // the bin's floor pattern, so the bin itself is only formed for the
@@ -694,19 +731,19 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         return p * inv_hq;
       };
       // with the KV heads fixed at 8 both masses are read in one batch first
-      float pm[2];
+      float pm[4];
       if constexpr (HK == 8) {
-        uint32_t ad[2];
+        uint32_t ad[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < 4; ++e) {
           const int mo = e * lpq + own_j;
           const int r = ((mo >> 3) << 2) | (mo & 3), h2 = (mo >> 2) & 1;
           ad[e] = lds_addr(pb + part_index(0, r, own_n + 32 * h2));
         }
-        f32x2 v[8];
-        read_partials_hk8(ad[0], ad[1], v);
+        f32x2 v[16];
+        read_partials_hk8x4(ad, v);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {   // heads in order 0..7, as mass() sums them
+        for (int e = 0; e < 4; ++e) {   // heads in order 0..7, as mass() sums them
           float p = v[4 * e].x;
           p += v[4 * e].y;
 #pragma unroll
@@ -763,7 +800,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
         if (hf == 0) pb[g * 32 + col] = blk;
         blk = 0.f;
         barrier_lds();
-        if (own_j == 0 && own_q < n) {
+        if (own_j == 0 && own_ok) {
           float p = 0.f;
           for (int gg = 0; gg < hkv; ++gg) p += pb[gg * 32 + own_n];
           p *= inv_hq;
@@ -784,7 +821,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   wait_vmem_all();
   if constexpr (CS) return;
   if constexpr (KB == 1) {
-    if (own_j == 0) {
+    if (owner_wave && own_j == 0) {
       rs.cnt[own_n] = r_cnt;
       rs.btau[own_n] = r_bt;
     }

@@ -264,7 +264,10 @@ def test_kl_key_gradient_lds_map_and_bounds():
 def test_pass2_partial_exchange_banks():
     """Partial masses of KV head g, register r, source lane l at word
     g*1088 + 68 r + l: the lane-major writes (one register per instruction)
-    and the row owners' reads (8 heads x 2 keys per lane) hit distinct banks."""
+    and the row owners' reads hit distinct banks, for both ownerships: with
+    the KV heads fixed at 8, waves 0..3 own 8 rows each (8 lanes a row, keys
+    m = 8 e + j, 4 per lane); otherwise every wave owns 32/Hkv rows (2 Hkv
+    lanes a row; here Hkv = 8: 4 rows, 16 lanes, keys m = 16 e + j)."""
     pitch, head = 68, 17 * 64
     for g, r in itertools.product(range(8), range(16)):
         addrs = [4 * (g * head + pitch * r + lane) for lane in range(64)]
@@ -278,3 +281,18 @@ def test_pass2_partial_exchange_banks():
             r, h2 = ((mo >> 3) << 2) | (mo & 3), (mo >> 2) & 1
             addrs.append(4 * (gg * head + pitch * r + own_n + 32 * h2))
         assert conflict_free(addrs, 4)
+    # owners with the KV heads fixed at 8: waves 0..3, 8 rows each, 8 lanes a
+    # row, key offsets m = 8 e + j
+    for w, e, gg in itertools.product(range(4), range(4), range(8)):
+        addrs = []
+        for lane in range(64):
+            own_n, own_j = 8 * w + lane // 8, lane % 8
+            mo = 8 * e + own_j
+            r, h2 = ((mo >> 3) << 2) | (mo & 3), (mo >> 2) & 1
+            addrs.append(4 * (gg * head + pitch * r + own_n + 32 * h2))
+        assert conflict_free(addrs, 4)
+    # every (row, key) of the tile has exactly one owner lane and entry
+    seen = set()
+    for w, lane, e in itertools.product(range(4), range(64), range(4)):
+        seen.add((8 * w + lane // 8, 8 * e + lane % 8))
+    assert seen == {(n, m) for n in range(32) for m in range(32)}
