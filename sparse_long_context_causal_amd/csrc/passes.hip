@@ -703,6 +703,9 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       for (int r = 0; r < 16; ++r) part[wb + kPartPitch * r] = pacc[r];
       barrier_lds();   // partial masses visible
       if (!owner_wave) continue;   // (uniform per wave)
+      // the owners' filter is a latency-bound chain that the other waves wait
+      // for at the next barrier: it gets the SIMD's issue slots first
+      if constexpr (HK == 8) __builtin_amdgcn_s_setprio(2);
       // ---- row owner: reduce over KV heads, filter, append, raise the bound
       // A mass passes the bound bin exactly when its bit pattern is at least
       // the bin's floor pattern, so the bin itself is only formed for the
@@ -787,6 +790,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
           else r_cge = cg;
         }
       }
+      if constexpr (HK == 8) __builtin_amdgcn_s_setprio(0);
     } else {
       // ---- key blocks of KB = 64 tokens = two key tiles
       float ps = 0.f;
