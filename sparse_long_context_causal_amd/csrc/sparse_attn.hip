@@ -620,6 +620,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     const unsigned valid = valid_next;
     // every load in flight belongs to this chunk
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // copying the chunk out and issuing the next one's loads go first among
+    // the SIMD's waves: the gather is bound by the bytes its waves keep in
+    // flight
+    __builtin_amdgcn_s_setprio(2);
     u32x4 kf[8];
     u32x2 vt[16];
     read_chunk(ka, va, kf, vt);
@@ -628,6 +632,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
       issue(off);
       if (ch + 2 < nch) fetch_ids(ch + 2, raw);
     }
+    __builtin_amdgcn_s_setprio(0);
     f32x4 sc[2];
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg) {
