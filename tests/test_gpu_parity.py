@@ -259,7 +259,7 @@ def test_sparse_attn_one_token_and_empty(gpu_lib):
             np.testing.assert_array_equal(out[i, h], x["v"][i // 2, h // 4])
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (8, 1)])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (8, 1), (64, 16), (16, 16)])
 @pytest.mark.parametrize("key_block", [1, 64])
 def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block, hq, hkv):
     """The MFMA path (bf16, d=128; 1, 2, 4 or 8 query heads per KV head) on

@@ -125,7 +125,7 @@ def test_windowed_key_block_supports(gpu_lib):
         assert float(np.max(np.abs(o2[i].astype(np.float64) - o_ref))) <= TOL_OUT["bf16"], f"row {i}"
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (4, 1), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (4, 1), (16, 2), (32, 16)])
 def test_windowed_other_head_layouts(gpu_lib, hq, hkv):
     """The windowed gather with 1, 2, 4 or 8 query heads per KV head and other
     KV head counts: two windows (8192 + 1808 tokens), against the one-pass
