@@ -448,6 +448,46 @@ __device__ __forceinline__ void read_chunk(const uint32_t (&ka)[4], const uint32
       : "memory");
 }
 
+// lane c of each row of 16 lanes, broadcast to the row (c a constant after
+// unrolling)
+__device__ __forceinline__ int row_bcast16(int x, int c) {
+  switch (c) {
+    case 0: return __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, false);
+    case 1: return __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, false);
+    case 3: return __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, false);
+    case 4: return __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, false);
+    case 5: return __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, false);
+    case 6: return __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, false);
+  }
+}
+
+// The two values of each lane pair l, l ^ 16 (W = 16) or l, l ^ 32 (W = 32),
+// as {value of the lower lane, value of the upper lane}: a permlane swap of
+// two copies of x, without an LDS round trip.
+template <int W>
+__device__ __forceinline__ f32x2 pair_xor(float x) {
+  const unsigned u = __float_as_uint(x);
+  if constexpr (W == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return f32x2{__uint_as_float(p[0]), __uint_as_float(p[1])};
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return f32x2{__uint_as_float(p[0]), __uint_as_float(p[1])};
+  }
+}
+template <int W>
+__device__ __forceinline__ float max_xor(float x) {
+  const f32x2 p = pair_xor<W>(x);
+  return fmaxf(p.x, p.y);
+}
+template <int W>
+__device__ __forceinline__ float sum_xor(float x) {
+  const f32x2 p = pair_xor<W>(x);
+  return p.x + p.y;
+}
+
 // broadcast of lane (l & ~3) | R to the 4 lanes of each quad
 template <int R>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -524,15 +564,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   // d-chunk m ^ 2((4c + q) & 7): byte offset in the row by the parity of c
   const unsigned xo0 = 16u * (unsigned)(m ^ (2 * q)), xo1 = 16u * (unsigned)(m ^ (8 + 2 * q));
 
-  // Raw token ids of chunk ch: raw[c] for the lane's DMA rows 4c + q and
-  // raw[8] for token lane%32 (single tokens), or the block ids of the
-  // chunk's two sets in raw[0] and raw[4] (key blocks: a set never
-  // straddles two blocks)
+  // Raw token ids of chunk ch. Single tokens: raw[0] in lane 16q + m holds
+  // the id of token 4(m & 7) + q, the row that lane group q takes in DMA
+  // instruction m & 7 (handed to the group's 16 lanes by a row broadcast
+  // from lane m), and raw[8] the id of token lane % 32. Key blocks: the
+  // block ids of the chunk's two sets in raw[0] and raw[4] (a set never
+  // straddles two blocks).
   auto fetch_ids = [&](int ch, int (&raw)[9]) {
     const int t0 = ch << 5;
     if constexpr (kUnitTokens) {
-#pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) raw[c8] = ids[min(t0 + 4 * c8 + q, lim)];
+      raw[0] = ids[min(t0 + 4 * (m & 7) + q, lim)];
       raw[8] = ids[min(t0 + (lane & 31), lim)];
     } else {
       raw[0] = ids[min(t0 / key_block, lim)];
@@ -557,11 +598,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   // chunk's validity bits (bit t: token t is a support key; uniform)
   auto rows_of = [&](int ch, const int (&raw)[9], unsigned (&off)[8]) -> unsigned {
     const int t0 = ch << 5;
-#pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
+    if constexpr (kUnitTokens) {
+      // the row of token 4(m & 7) + q (row i for a token that weighs 0),
+      // then row-broadcast from lane c of each 16-lane group for instruction c
       int r;
-      const bool ok = token_row(t0, 4 * c8 + q, kUnitTokens ? raw[c8] : raw[4 * (c8 >> 2)], r);
-      off[c8] = ((unsigned)(ok ? r : i) << row_shift) + ((c8 & 1) ? xo1 : xo0);
+      const int rd = token_row(t0, 4 * (m & 7) + q, raw[0], r) ? r : i;
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8)
+        off[c8] = ((unsigned)row_bcast16(rd, c8) << row_shift) + ((c8 & 1) ? xo1 : xo0);
+    } else {
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) {
+        int r;
+        const bool ok = token_row(t0, 4 * c8 + q, raw[4 * (c8 >> 2)], r);
+        off[c8] = ((unsigned)(ok ? r : i) << row_shift) + ((c8 & 1) ? xo1 : xo0);
+      }
     }
     int r;
     int own = raw[8];
@@ -653,8 +704,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     }
     float smax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
-    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+    smax = max_xor<32>(max_xor<16>(smax));
     const float mnew = fmaxf(mrun, smax * c);
     if (__ballot(mnew != mrun)) {   // a head's maximum moved: rescale
       const float alpha = mnew == mrun ? 1.0f : fast_exp2(mrun - mnew);
@@ -691,8 +741,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
                                                         __builtin_bit_cast(bf16x8, vv), acc[bb], 0, 0, 0);
     }
   }
-  float l = lrun + __shfl_xor(lrun, 16, 64);   // every lane: head lane%G
-  l += __shfl_xor(l, 32, 64);
+  const float l = sum_xor<32>(sum_xor<16>(lrun));   // every lane: head lane%G
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   // this window's LSE of head lane%G (log2 units)
   const float lw = l > 0.f ? mrun + log2f(l) : -INFINITY;
@@ -752,7 +801,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
       o1 = t[1] + t[3];
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] += __shfl_xor(t[r], G == 4 ? 16 : 32, 64);
+      for (int r = 0; r < 4; ++r) t[r] = G == 4 ? sum_xor<16>(t[r]) : sum_xor<32>(t[r]);
       o0 = rsel ? t[2] : t[0];
       o1 = rsel ? t[3] : t[1];
     }
