@@ -228,7 +228,7 @@ __device__ __forceinline__ void shared_attn_tile(
     float smax = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) smax = fmaxf(smax, x[r]);
-    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+    smax = max_xor<32>(smax);
     const float mnew = fmaxf(mrun, smax * c);
     if (__ballot(mnew != mrun)) {   // a query's maximum moved: rescale
       const float alpha = mnew == mrun ? 1.0f : fast_exp2(mrun - mnew);
@@ -276,7 +276,7 @@ __device__ __forceinline__ void shared_attn_tile(
       }
     }
   }
-  const float l = lrun + __shfl_xor(lrun, 32, 64);
+  const float l = sum_xor<32>(lrun);
   if (qrow >= n) return;   // (no barrier follows inside the tile)
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   // O^T register r of tile dt: d = 32 dt + 8(r/4) + 4 hl + r%4
@@ -392,9 +392,15 @@ __global__ __launch_bounds__(512) void indexer_shared_kernel(
             csum += (key <= qq) ? p : 0.f;
           }
         }
-        csum += __shfl_xor(csum, 32, 64);          // the other half's queries
-#pragma unroll
-        for (int sh = 1; sh < 32; sh <<= 1) csum += __shfl_xor(csum, sh, 64);
+        csum = sum_xor<32>(csum);   // the other half's queries
+        // then the 32 keys: pairs at distance 1, 2, 4, 8 (DPP; once a group
+        // holds equal values, its mirror image pairs it with the next group)
+        // and 16
+        csum += dpp_f32<kDppQuadXor1>(csum);
+        csum += dpp_f32<kDppQuadXor2>(csum);
+        csum += dpp_f32<kDppRowHalfMirror>(csum);
+        csum += dpp_f32<kDppRowMirror>(csum);
+        csum = sum_xor<16>(csum);
         usum += csum;
       }
       if (lane == 0) ix.score[u] = usum * inv_rows;

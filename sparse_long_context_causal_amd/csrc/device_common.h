@@ -286,8 +286,59 @@ __device__ __forceinline__ void score_tile(f32x16& acc, const uint4 (&kc)[NC],
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
 // -------------------------------------------------------------- wave helpers
-__device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
-__device__ __forceinline__ int xor32i(int v) { return __shfl_xor(v, 32, 64); }
+// DPP lane permutations within rows of 16 lanes
+constexpr int kDppRowMirror = 0x140;       // lane i <-> 15 - i
+constexpr int kDppRowHalfMirror = 0x141;   // lane i <-> 7 - i within each 8
+constexpr int kDppQuadXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;         // quad_perm [1,0,3,2]
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+// The values of x in lanes l and l ^ W (W = 16 or 32) as {lo, hi}, lo from
+// the lower lane of the pair: a permlane swap of two copies of x, in the
+// VALU (no LDS round trip). Every use below is symmetric in the pair or
+// picks the partner by comparing with its own value.
+template <int W>
+__device__ __forceinline__ void lane_pair(unsigned u, unsigned& lo, unsigned& hi) {
+  static_assert(W == 16 || W == 32, "permlane swaps exchange rows of 16 or halves of 32");
+  if constexpr (W == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = p[0];
+    hi = p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = p[0];
+    hi = p[1];
+  }
+}
+template <int W>
+__device__ __forceinline__ float max_xor(float x) {
+  unsigned lo, hi;
+  lane_pair<W>(__float_as_uint(x), lo, hi);
+  return fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+}
+template <int W>
+__device__ __forceinline__ float sum_xor(float x) {
+  unsigned lo, hi;
+  lane_pair<W>(__float_as_uint(x), lo, hi);
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+// the value of x in lane l ^ W: the member of the pair that is not this
+// lane's own (when both are equal, either)
+template <int W>
+__device__ __forceinline__ unsigned partner_u32(unsigned u) {
+  unsigned lo, hi;
+  lane_pair<W>(u, lo, hi);
+  return lo == u ? hi : lo;
+}
+__device__ __forceinline__ float xor32f(float v) { return __uint_as_float(partner_u32<32>(__float_as_uint(v))); }
+__device__ __forceinline__ int xor32i(int v) { return (int)partner_u32<32>((unsigned)v); }
 
 // Generic element loads for the VALU kernels.
 __device__ __forceinline__ float load_elem(const float* p) { return *p; }

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
     }
   }
   // ---- per-row KL (waves 0 and 1) and dq (waves 0, 1)
-  float klq = klacc + __shfl_xor(klacc, 32, 64);
+  float klq = sum_xor<32>(klacc);
   float* red = reinterpret_cast<float*>(smem + kKlRed);
   if (wave == 1 && hf == 0) red[col] = klq;
   barrier_lds();

@@ -52,15 +52,6 @@ namespace amtk {
 // Column-sum mode: tiles of per-wave key sums held in LDS before a fold.
 constexpr int kCsRing = 32;
 
-// DPP lane permutations within rows of 16 lanes
-constexpr int kDppRowMirror = 0x140;       // lane i <-> 15 - i
-constexpr int kDppRowHalfMirror = 0x141;   // lane i <-> 7 - i within each 8
-constexpr int kDppQuadXor2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr int kDppQuadXor1 = 0xB1;         // quad_perm [1,0,3,2]
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
 
 // Mass bins of the filter (kFBins, 8 per octave), u16 counts packed two
 // per LDS word.

@@ -463,31 +463,6 @@ __device__ __forceinline__ int row_bcast16(int x, int c) {
   }
 }
 
-// The two values of each lane pair l, l ^ 16 (W = 16) or l, l ^ 32 (W = 32),
-// as {value of the lower lane, value of the upper lane}: a permlane swap of
-// two copies of x, without an LDS round trip.
-template <int W>
-__device__ __forceinline__ f32x2 pair_xor(float x) {
-  const unsigned u = __float_as_uint(x);
-  if constexpr (W == 16) {
-    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return f32x2{__uint_as_float(p[0]), __uint_as_float(p[1])};
-  } else {
-    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return f32x2{__uint_as_float(p[0]), __uint_as_float(p[1])};
-  }
-}
-template <int W>
-__device__ __forceinline__ float max_xor(float x) {
-  const f32x2 p = pair_xor<W>(x);
-  return fmaxf(p.x, p.y);
-}
-template <int W>
-__device__ __forceinline__ float sum_xor(float x) {
-  const f32x2 p = pair_xor<W>(x);
-  return p.x + p.y;
-}
-
 // broadcast of lane (l & ~3) | R to the 4 lanes of each quad
 template <int R>
 __device__ __forceinline__ float quad_bcast(float x) {
