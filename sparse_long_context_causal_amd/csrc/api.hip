@@ -64,7 +64,7 @@ int check_support(const amtk_support_desc* sp) {
 }
 
 struct Layout {
-  size_t cand, count, bin, lse, ovf_count, ovf_list, scratch, colsum, total;
+  size_t cand, count, bin, lse, ovf_count, ovf_list, scratch, colsum, kops, kops_bytes, total;
   int cap, units_max;
 };
 
@@ -98,6 +98,8 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
   L.ovf_count = off;  off = round_up(off + sizeof(int));
   L.ovf_list = off;   off = round_up(off + n * sizeof(int));
   L.scratch = off;    off = round_up(off + (size_t)amtk::kFallbackSlots * L.units_max * sizeof(float));
+  L.kops_bytes = amtk::pass2_key_operand_bytes(s, sp.key_block);
+  L.kops = off;       off = round_up(off + L.kops_bytes);
   L.colsum = 0;
   L.total = off;
   return L;
@@ -112,6 +114,7 @@ CandidatePool pool_of(void* ws, const Layout& L) {
   p.ovf_count = reinterpret_cast<int*>(b + L.ovf_count);
   p.ovf_list = reinterpret_cast<int*>(b + L.ovf_list);
   p.scratch = reinterpret_cast<float*>(b + L.scratch);
+  p.kops = L.kops_bytes ? b + L.kops : nullptr;
   p.cap = L.cap;
   p.slots = amtk::kFallbackSlots;
   return p;

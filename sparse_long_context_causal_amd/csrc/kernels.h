@@ -29,6 +29,7 @@ struct CandidatePool {
   int* ovf_count;   // [1] rows whose pool overflowed
   int* ovf_list;    // [n] their row ids
   float* scratch;   // [slots][units_max] dense rows for the overflow path
+  void* kops;       // key tiles in MFMA operand order (pass2_key_operand_bytes)
   int cap;          // capacity per row
   int slots;        // overflow rows processed concurrently
 };
@@ -37,6 +38,11 @@ constexpr int kMaxBudget = 8192;      // largest k the select kernel sorts in LD
 constexpr size_t kLdsBytesPerCu = 160 * 1024;   // LDS of one gfx950 CU (one workgroup's maximum)
 constexpr int kMaxQRow = 8192;        // largest Hq*d held in LDS by the overflow path
 constexpr int kFallbackSlots = 128;   // concurrent overflow rows
+
+// Bytes of pass 2's copy of the keys in MFMA operand order (8 KV heads, bf16,
+// d = 128, one support per query; 0 for other shapes, which stage key tiles
+// through LDS instead).
+size_t pass2_key_operand_bytes(const LayerShape& s, int key_block);
 
 // Per-head causal row log-sum-exp, lse[h][i] (natural log). Also zeroes
 // pool.ovf_count for the pass that follows.

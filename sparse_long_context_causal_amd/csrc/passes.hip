@@ -503,7 +503,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ lse, int n,
     int hkv_arg, float c, float inv_hq, int budget, uint2* __restrict__ cand, int cap,
     int* __restrict__ cand_count, int* __restrict__ row_bin, int* __restrict__ ovf_count,
-    int* __restrict__ ovf_list, float* __restrict__ colsum) {
+    int* __restrict__ ovf_list, float* __restrict__ colsum, const uint4* __restrict__ kops) {
   static_assert(!CS || KB == 1, "column sums are per token");
   const int hkv = HK ? HK : hkv_arg;
   typedef KTile<T, D> KT;
@@ -530,7 +530,12 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
 
   KLane<T, D> kl;
   kl.init(lane, hkv);
-  kl.issue(K, n, hkv, g, 0, slot);
+  // kops (8 KV heads, bf16, d = 128, one support per query): every key tile
+  // is already stored in MFMA operand order, and tile t+1 goes from memory
+  // straight into the registers once tile t's last MFMAs have read them
+  constexpr bool kDirect = HK == 8 && KB == 1 && !CS && std::is_same<T, bf16_t>::value && D == 128;
+  const uint4* kop = kDirect ? kops + (size_t)g * ntiles * (NC * 64) + lane : nullptr;
+  if constexpr (!kDirect) kl.issue(K, n, hkv, g, 0, slot);
   for (int t = threadIdx.x; t < 32 * kFBinWords; t += nthreads) hist[t] = 0u;
   if (threadIdx.x < 32) {
     rs.cnt[threadIdx.x] = 0;
@@ -610,10 +615,17 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   };
   // head-summed probabilities of the current key tile for this lane's query
   // (head 0's scores are already in a0)
-  auto tile_mass = [&](bool diag, float (&pacc)[16]) {
+  auto load_direct = [&](int kt) __attribute__((always_inline)) {
+    const uint4* src = kop + (size_t)kt * (NC * 64);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kc[c] = src[64 * c];
+  };
+  // after_mfma runs once the tile's last MFMA has been issued (key tile free)
+  auto tile_mass = [&](bool diag, float (&pacc)[16], auto after_mfma) {
     if constexpr (kInterleave) {
 #pragma unroll
       for (int h = 0; h + 1 < G; ++h) head_step((h & 1) ? a0 : a1, qc[h + 1], (h & 1) ? a1 : a0, h, pacc);
+      after_mfma();
       head_exps(((G - 1) & 1) ? a1 : a0, G - 1, pacc);
     } else {
 #pragma unroll
@@ -634,13 +646,18 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   // candidates appended, candidates in bins >= the bound bin, the bound bin
   // and the count of that bin itself
   int r_cnt = 0, r_cge = 0, r_bt = 0, r_hb = 0;
+  if constexpr (kDirect) load_direct(0);
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
-    load_k(kt);
+    if constexpr (!kDirect) load_k(kt);
     score_tile<T, NC>(a0, kc, qc[0]);
     float pacc[16];
-    tile_mass(diag, pacc);
+    tile_mass(diag, pacc, [&]() __attribute__((always_inline)) {
+      if constexpr (kDirect) {
+        if (kt < qt) load_direct(kt + 1);
+      }
+    });
 
     if constexpr (CS) {
       // ---- column sums: each wave sums its heads' masses over the tile's
@@ -833,6 +850,23 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   }
 }
 
+// Key tiles in MFMA operand order (8 KV heads, bf16, d = 128): entry
+// ((g * T + t) * 8 + c) * 64 + l is the 16-byte chunk c of lane l's operand
+// of tile t of KV head g, i.e. K[32 t + l % 32][g][64 (l / 32) + 8 c ..]
+// (rows past n repeat row n - 1), so a wave loads one tile as 8 fully
+// contiguous 1 KiB reads.
+__global__ __launch_bounds__(256) void key_operands_kernel(const bf16_t* __restrict__ K,
+                                                           uint4* __restrict__ kops, int n,
+                                                           int ntiles) {
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (size_t)8 * ntiles * 512) return;
+  const int l = (int)(id & 63), c = (int)((id >> 6) & 7);
+  const size_t gt = id >> 9;
+  const int t = (int)(gt % (size_t)ntiles), g = (int)(gt / (size_t)ntiles);
+  const int row = min(t * 32 + (l & 31), n - 1);
+  kops[id] = *reinterpret_cast<const uint4*>(K + ((size_t)row * 8 + g) * 128 + 64 * (l >> 5) + 8 * c);
+}
+
 // ------------------------------------------------------------ dispatching
 template <typename T, int D, int G>
 static hipError_t run_pass1(const LayerShape& s, const void* q, const void* k, float* lse,
@@ -850,29 +884,43 @@ static hipError_t run_pass1(const LayerShape& s, const void* q, const void* k, f
   return hipGetLastError();
 }
 
+// key_slots false: the direct path (key tiles straight into registers)
 template <typename T, int D>
-static size_t pass2_lds_bytes(int hkv, int key_block) {
+static size_t pass2_lds_bytes(int hkv, int key_block, bool key_slots = true) {
   size_t b = 32 * kFBinWords * sizeof(unsigned) + sizeof(RowState);
   b += 2 * ((key_block == 1) ? (size_t)hkv * kPartHead : (size_t)hkv * 32) * sizeof(float);
   b = (b + 1023) & ~(size_t)1023;   // key slots on a 1 KiB boundary
-  b += (size_t)hkv * KTile<T, D>::kBytes;
+  if (key_slots) b += (size_t)hkv * KTile<T, D>::kBytes;
   return b;
+}
+
+size_t pass2_key_operand_bytes(const LayerShape& s, int key_block) {
+  if (s.dtype != kBF16 || s.d != 128 || s.hkv != 8 || key_block != 1) return 0;
+  return (size_t)((s.n + 31) / 32) * 32 * 8 * 128 * sizeof(bf16_t);
 }
 
 template <typename T, int D, int G, int KB>
 static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, const void* k,
                             const float* lse, const CandidatePool& pool, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
-  const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB);
+  const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB, pass2_key_operand_bytes(s, KB) == 0);
   auto kern = s.hkv == 8 ? pass2_filter_kernel<T, D, G, KB, 8, false>
                          : pass2_filter_kernel<T, D, G, KB, 0, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  uint4* kops = nullptr;
+  if (pass2_key_operand_bytes(s, KB)) {   // the keys in operand order, for this call's K
+    kops = static_cast<uint4*>(pool.kops);
+    if (!kops) return hipErrorInvalidValue;
+    const size_t total = (size_t)8 * ntiles * 512;
+    hipLaunchKernelGGL(key_operands_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const bf16_t*>(k), kops, s.n, ntiles);
+  }
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
                      s.scale * kLog2e, 1.0f / (float)s.hq, budget, pool.cand, pool.cap, pool.count,
-                     pool.bin, pool.ovf_count, pool.ovf_list, nullptr);
+                     pool.bin, pool.ovf_count, pool.ovf_list, nullptr, kops);
   return hipGetLastError();
 }
 
@@ -889,7 +937,7 @@ static hipError_t run_pass2_colsum(const LayerShape& s, const void* q, const voi
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
                      s.scale * kLog2e, 1.0f / (float)s.hq, 0, nullptr, 0, nullptr, nullptr, nullptr,
-                     nullptr, colsum);
+                     nullptr, colsum, nullptr);
   return hipGetLastError();
 }
 

@@ -296,3 +296,41 @@ def test_pass2_partial_exchange_banks():
     for w, lane, e in itertools.product(range(4), range(64), range(4)):
         seen.add((8 * w + lane // 8, 8 * e + lane % 8))
     assert seen == {(n, m) for n in range(32) for m in range(32)}
+
+
+# ------------------------------------------- pass 2's key operand copy
+def test_pass2_key_operand_copy():
+    """Pass 2 with 8 KV heads, bf16, d = 128 loads its key tiles from a copy of
+    K in MFMA operand order (passes.hip key_operands_kernel): entry
+    ((g T + t) 8 + c) 64 + l holds the 16-byte chunk c of lane l's operand of
+    tile t of KV head g, and wave g reads tile t as 8 loads of 64 consecutive
+    entries (entry t*512 + 64 c + l for lane l). Every lane must get the
+    operand chunk the LDS staging gives it (row l % 32, chunk (l/32) nc + c of
+    the row's 16 chunks), every chunk of every padded tile must appear
+    exactly once, and rows past n repeat row n - 1."""
+    L = KLayout(128, 2)
+    hkv, nc = 8, 8
+    for n in (1, 31, 33, 100):
+        ntiles = (n + 31) // 32
+        seen = set()
+        for idx in range(hkv * ntiles * 512):             # the copy kernel's thread ids
+            l, c, gt = idx & 63, (idx >> 6) & 7, idx >> 9
+            t, g = gt % ntiles, gt // ntiles
+            row = min(t * 32 + (l & 31), n - 1)
+            chunk = 8 * (l >> 5) + c                     # d = 64 (l/32) + 8 c, in 16-byte units
+            key = (g, t * 32 + (l & 31), chunk)
+            assert key not in seen
+            seen.add(key)
+            if t * 32 + (l & 31) >= n:
+                assert row == n - 1
+            # the wave's read of tile t, instruction c, lane l hits entry idx
+            assert ((g * ntiles + t) * 8 + c) * 64 + l == idx
+            assert (row % 32 == (l & 31)) or t * 32 + (l & 31) >= n
+            assert (l & 31, chunk) == (l & 31, (l >> 5) * L.nc + c)
+        assert len(seen) == hkv * ntiles * 32 * 16
+        # the workspace figure (pass2_key_operand_bytes)
+        assert hkv * ntiles * 512 * 16 == ntiles * 32 * 8 * 128 * 2
+    # each load instruction reads 64 consecutive 16-byte entries: 1 KiB contiguous
+    for c in range(nc):
+        addrs = [16 * (64 * c + l) for l in range(64)]
+        assert addrs == list(range(addrs[0], addrs[0] + 1024, 16))
