@@ -647,6 +647,115 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   // and the count of that bin itself
   int r_cnt = 0, r_cge = 0, r_bt = 0, r_hb = 0;
   if constexpr (kDirect) load_direct(0);
+  if constexpr (kDirect) {
+    // ---- 8 KV heads, bf16, d = 128, one support per query. Waves 0..3 own
+    // 8 rows each; wave w + 4 (which shares wave w's SIMD) sums, after
+    // producing tile t+1, the 8 KV heads' partial masses of tile t for
+    // wave w's rows into a small LDS buffer, and wave w filters tile t from
+    // those sums after the next barrier (a lag of one tile: partial
+    // buffers are rewritten two tiles later, sum buffers two filters
+    // later). The owners' filter, which the other waves wait for at every
+    // barrier, then reads 4 sums per lane instead of 32 partial masses.
+    float* const sums = part + 2 * part_floats;   // [2][4 owners][4 keys][64 lanes]
+    const int ow = wave & 3;                        // the owner this wave serves or is
+    const int s_n = ow * 8 + (lane >> 3), s_j = lane & 7;   // the owner's lane layout
+    // LDS byte addresses as a per-tile uniform base plus a lane offset
+    const uint32_t part_lds = lds_addr(part), sums_lds = lds_addr(sums);
+    uint32_t hs_off[4];   // head 0's partial of keys 8e + s_j of row s_n, in a buffer
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int mo = e * 8 + s_j;
+      const int r = ((mo >> 3) << 2) | (mo & 3), h2 = (mo >> 2) & 1;
+      hs_off[e] = 4u * (uint32_t)part_index(0, r, s_n + 32 * h2);
+    }
+    const uint32_t sum_off = 4u * (uint32_t)(ow * 256 + lane);
+    auto produce = [&](int kt) __attribute__((always_inline)) {
+      score_tile<T, NC>(a0, kc, qc[0]);
+      float pacc[16];
+      tile_mass(kt == qt, pacc, [&]() __attribute__((always_inline)) {
+        if (kt < qt) load_direct(kt + 1);
+      });
+      const int wb = (kt & 1) * part_floats + part_index(g, 0, lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[wb + kPartPitch * r] = pacc[r];
+    };
+    // the mass of keys 8e + s_j of row s_n of tile ft: the 8 KV heads'
+    // partial masses summed in order 0..7, times 1/hq
+    auto head_sums = [&](int ft) __attribute__((always_inline)) {
+      const uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(part_lds + (uint32_t)((ft & 1) * part_floats * 4)));
+      float* sb = sums + (ft & 1) * 1024 + ow * 256 + lane;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; e2 += 2) {   // two keys per round trip
+        f32x2 v[8];
+        read_partials_hk8(pb + hs_off[e2], pb + hs_off[e2 + 1], v);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float p = v[4 * u].x;
+          p += v[4 * u].y;
+#pragma unroll
+          for (int j = 1; j < 4; ++j) {
+            p += v[4 * u + j].x;
+            p += v[4 * u + j].y;
+          }
+          sb[64 * (e2 + u)] = p * inv_hq;
+        }
+      }
+    };
+    // the owner's filter of tile ft (see the generic loop below)
+    auto filter = [&](int ft) __attribute__((always_inline)) {
+      // the owners' filter is a latency-bound chain that the other waves
+      // wait for at the next barrier: it gets the SIMD's issue slots first
+      __builtin_amdgcn_s_setprio(2);
+      const int k0 = ft << 5;
+      const bool diag = ft == qt;
+      const float* sb = sums + (ft & 1) * 1024 + ow * 256 + lane;
+      float pm[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pm[e] = sb[64 * e];
+      const int pos0 = r_cnt;
+      const unsigned thr = filter_bin_floor_bits(r_bt);
+      int pos = pos0;
+      const bool live = own_ok && pos <= cap;
+      int in_bt = 0;   // this tile's appends that fall in the bound's own bin
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int mo = e * 8 + own_j;
+        const float p = pm[e];
+        const unsigned bits = __float_as_uint(p);
+        const int key = k0 + mo;
+        const bool flag = own_ok && bits >= thr && (!diag || key <= own_q);
+        const unsigned long long m = __ballot(flag) & grp_mask;
+        const int bin = filter_bin(p);
+        if (flag) {
+          const int at = pos + __popcll(m & below);
+          if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(bits, (unsigned)key);
+          if (live) lds_add(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
+        }
+        in_bt += __popcll(__ballot(flag && bin == r_bt) & grp_mask);
+        pos += __popcll(m);
+      }
+      if (pos != pos0) {
+        const int cg = r_cge + (pos - pos0);
+        r_cnt = pos;
+        if (pos <= cap) {
+          r_hb += in_bt;
+          if (r_bt < kFBins - 1 && cg - r_hb >= budget) raise_bound_regs(own_hist, budget, cg, r_cge, r_bt, r_hb);
+          else r_cge = cg;
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    for (int kt = 0; kt <= qt; ++kt) {
+      produce(kt);
+      if (!owner_wave && kt > 0) head_sums(kt - 1);
+      barrier_lds();   // partial masses of tile kt, sums of tile kt - 1 visible
+      if (owner_wave && kt > 0) filter(kt - 1);
+    }
+    if (!owner_wave) head_sums(qt);
+    barrier_lds();     // sums of the last tile
+    if (owner_wave) filter(qt);
+  } else
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
@@ -884,14 +993,15 @@ static hipError_t run_pass1(const LayerShape& s, const void* q, const void* k, f
   return hipGetLastError();
 }
 
-// key_slots false: the direct path (key tiles straight into registers)
+// direct: key tiles straight into registers (no key slots), with the head
+// sums' buffer of the 8-KV-head path
 template <typename T, int D>
-static size_t pass2_lds_bytes(int hkv, int key_block, bool key_slots = true) {
+static size_t pass2_lds_bytes(int hkv, int key_block, bool direct = false) {
   size_t b = 32 * kFBinWords * sizeof(unsigned) + sizeof(RowState);
   b += 2 * ((key_block == 1) ? (size_t)hkv * kPartHead : (size_t)hkv * 32) * sizeof(float);
+  if (direct) return b + 2 * 4 * 4 * 64 * sizeof(float);
   b = (b + 1023) & ~(size_t)1023;   // key slots on a 1 KiB boundary
-  if (key_slots) b += (size_t)hkv * KTile<T, D>::kBytes;
-  return b;
+  return b + (size_t)hkv * KTile<T, D>::kBytes;
 }
 
 size_t pass2_key_operand_bytes(const LayerShape& s, int key_block) {
@@ -903,7 +1013,7 @@ template <typename T, int D, int G, int KB>
 static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, const void* k,
                             const float* lse, const CandidatePool& pool, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
-  const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB, pass2_key_operand_bytes(s, KB) == 0);
+  const size_t lds = pass2_lds_bytes<T, D>(s.hkv, KB, pass2_key_operand_bytes(s, KB) != 0);
   auto kern = s.hkv == 8 ? pass2_filter_kernel<T, D, G, KB, 8, false>
                          : pass2_filter_kernel<T, D, G, KB, 0, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
