@@ -631,6 +631,7 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (h > 0) score_tile<T, NC>(a0, kc, qc[h]);
+        if (h == G - 1) after_mfma();   // (head 0's MFMAs ran before: G = 1 too)
         head_exps(a0, h, pacc);
       }
     }

@@ -61,6 +61,7 @@ def _full_check(amtk, x, dtype, k, key_block=1, rows=None, cap=0):
     (161, 8, 1, 64, "bf16", 11),    # G = 8, d = 64
     (90, 4, 2, 128, "f32", 6),      # fp32, d = 128
     (110, 8, 4, 128, "bf16", 8),    # G = 2, four KV heads
+    (99, 8, 8, 128, "bf16", 10),    # G = 1 with eight KV heads (key tiles loaded straight to registers)
 ])
 def test_small_shapes_all_rows(gpu_lib, n, hq, hkv, d, dtype, k):
     x = random_inputs(n, hq, hkv, d, dtype, seed=n * 7 + hq, sink=True)
@@ -180,6 +181,19 @@ def test_overflow_path_gives_same_supports(gpu_lib):
     assert same > 0.98
     check_outputs_on_gpu_support(b["out"], None, layer, np.arange(0, 260, 7), b["idx"],
                                  b["count"], 1, "bf16")
+
+
+def test_overflow_path_eight_kv_heads(gpu_lib):
+    """The same with 8 KV heads, bf16, d = 128 (pass 2's key tiles come from the
+    workspace copy in operand order; rows whose pools overflow are redone densely)."""
+    x = random_inputs(230, 32, 8, 128, "bf16", seed=13, sink=True)
+    a = _run_oracle_prefill(gpu_lib, x, "bf16", 12)
+    b = _run_oracle_prefill(gpu_lib, x, "bf16", 12, cap=13)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    check_support_rows(b["idx"], b["count"], layer, np.arange(230), 12)
+    assert np.array_equal(a["count"], b["count"])
+    same = np.mean([np.array_equal(a["idx"][i], b["idx"][i]) for i in range(230)])
+    assert same > 0.98
 
 
 def test_overflow_rows_are_reported(gpu_lib):
