@@ -403,6 +403,7 @@ constexpr int kTileBytes = 8192;   // 32 rows of 256 bytes: keys or values of on
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the other counters left at their maximum)
 constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
@@ -448,6 +449,31 @@ __device__ __forceinline__ void read_chunk(const uint32_t (&ka)[4], const uint32
       : "memory");
 }
 
+// The same for a chunk of 16 tokens (one set): 4 key fragments, 8 value
+// fragments.
+__device__ __forceinline__ void read_chunk16(const uint32_t (&ka)[4], const uint32_t (&va)[8],
+                                             u32x4 (&kf)[4], u32x2 (&vt)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(vt[0]), "=&v"(vt[1]),
+        "=&v"(vt[2]), "=&v"(vt[3]), "=&v"(vt[4]), "=&v"(vt[5]), "=&v"(vt[6]), "=&v"(vt[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+      : "memory");
+}
+
 // lane c of each row of 16 lanes, broadcast to the row (c a constant after
 // unrolling)
 __device__ __forceinline__ int row_bcast16(int x, int c) {
@@ -488,8 +514,10 @@ __device__ __forceinline__ void head_factors(float x, float (&f)[4]) {
   }
 }
 
-template <bool kUnitTokens, int G>   // kUnitTokens true: key_block == 1; false: key_block % 16 == 0
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_mfma_kernel(
+// kTok: tokens per chunk, 32 (two sets of 16) or 16 (one set; half the LDS
+// per wave, so more waves per CU)
+template <bool kUnitTokens, int G, int kTok>   // kUnitTokens true: key_block == 1; false: key_block % 16 == 0
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ? 4 : 3))) void sparse_attn_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
     float* __restrict__ lse_out, int n, int hkv_log2, int key_block, int max_units, float c,
@@ -499,7 +527,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   const int hkv = 1 << hkv_log2;   // a power of two: rows and heads by shifts
   const int HQ = hkv * G;
   const unsigned row_shift = (unsigned)hkv_log2 + 8u;   // bytes of one token, all KV heads: hkv * 256
-  __shared__ __align__(256) unsigned char smem[2 * kTileBytes];   // keys, values of a chunk
+  static_assert(kTok == 16 || kTok == 32, "chunks of one or two sets of 16 tokens");
+  constexpr int kSets = kTok / 16, kDma = kTok / 4;   // DMA instructions per chunk (keys or values)
+  constexpr int kBuf = kTok * 256;                     // bytes of a chunk's keys (or values)
+  __shared__ __align__(256) unsigned char smem[2 * kBuf];   // keys, values of a chunk
   const int lane = threadIdx.x;
   const int i = n - 1 - (int)(blockIdx.x >> hkv_log2);   // longest rows first
   const int g = (int)(blockIdx.x & (unsigned)(hkv - 1));
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   const bool merge = nwin > 0 && win > 0;
   const int lim = max_units - 1 - s0;   // last readable position after the shift
   const int total = cnt * key_block;
-  const int nch = (total + 31) >> 5;
+  const int nch = (total + kTok - 1) / kTok;
   if (nch == 0) {   // empty support: zero output, LSE -inf
     for (int e = lane; e < G * D; e += 64) O[((size_t)i * HQ + G * g) * D + e] = 0.f;
     if (lse_out && lane < G) lse_out[(size_t)(G * g + lane) * n + i] = -INFINITY;
@@ -532,7 +563,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   }
   const int32_t* ids = idx + (size_t)i * max_units + s0;
   unsigned char* kbuf = smem;
-  unsigned char* vbuf = smem + kTileBytes;
+  unsigned char* vbuf = smem + kBuf;
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K) + g * (D * 2);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V) + g * (D * 2);
   // DMA: lane 16q + m takes piece m of row 4c + q (c = 0..7), which holds
@@ -546,13 +577,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   // block ids of the chunk's two sets in raw[0] and raw[4] (a set never
   // straddles two blocks).
   auto fetch_ids = [&](int ch, int (&raw)[9]) {
-    const int t0 = ch << 5;
+    const int t0 = ch * kTok;
     if constexpr (kUnitTokens) {
-      raw[0] = ids[min(t0 + 4 * (m & 7) + q, lim)];
-      raw[8] = ids[min(t0 + (lane & 31), lim)];
+      raw[0] = ids[min(t0 + 4 * (m & (kDma - 1)) + q, lim)];
+      raw[8] = ids[min(t0 + (lane & (kTok - 1)), lim)];
     } else {
       raw[0] = ids[min(t0 / key_block, lim)];
-      raw[4] = ids[min((t0 + 16) / key_block, lim)];
+      if constexpr (kSets == 2) raw[4] = ids[min((t0 + 16) / key_block, lim)];
     }
   };
   // key/value row of token rr of the chunk starting at t0, given its raw id
@@ -572,18 +603,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
   // global byte offsets of the lane's 8 DMA pieces of chunk ch, and the
   // chunk's validity bits (bit t: token t is a support key; uniform)
   auto rows_of = [&](int ch, const int (&raw)[9], unsigned (&off)[8]) -> unsigned {
-    const int t0 = ch << 5;
+    const int t0 = ch * kTok;
     if constexpr (kUnitTokens) {
-      // the row of token 4(m & 7) + q (row i for a token that weighs 0),
+      // the row of token 4(m mod kDma) + q (row i for a token that weighs 0),
       // then row-broadcast from lane c of each 16-lane group for instruction c
       int r;
-      const int rd = token_row(t0, 4 * (m & 7) + q, raw[0], r) ? r : i;
+      const int rd = token_row(t0, 4 * (m & (kDma - 1)) + q, raw[0], r) ? r : i;
 #pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8)
+      for (int c8 = 0; c8 < kDma; ++c8)
         off[c8] = ((unsigned)row_bcast16(rd, c8) << row_shift) + ((c8 & 1) ? xo1 : xo0);
     } else {
 #pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) {
+      for (int c8 = 0; c8 < kDma; ++c8) {
         int r;
         const bool ok = token_row(t0, 4 * c8 + q, raw[4 * (c8 >> 2)], r);
         off[c8] = ((unsigned)(ok ? r : i) << row_shift) + ((c8 & 1) ? xo1 : xo0);
@@ -592,16 +623,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     int r;
     int own = raw[8];
     if constexpr (!kUnitTokens) {   // a select, not an indexed access (which would go to scratch)
-      const int lo = raw[0], hi = raw[4];
-      own = (lane & 16) ? hi : lo;
+      if constexpr (kSets == 2) own = (lane & 16) ? raw[4] : raw[0];
+      else own = raw[0];
     }
-    const bool okt = token_row(t0, lane & 31, own, r);
+    // (16-token chunks: lanes 16..31 repeat tokens 0..15, so the ballot's
+    // upper half repeats its lower half)
+    const bool okt = token_row(t0, lane & (kTok - 1), own, r);
     return (unsigned)__ballot(okt);   // lanes 0..31: tokens 0..31
   };
   const uint32_t kb_lds = lds_addr(kbuf), vb_lds = lds_addr(vbuf);
   auto issue = [&](const unsigned (&off)[8]) {
 #pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
+    for (int c8 = 0; c8 < kDma; ++c8) {
       __builtin_amdgcn_global_load_lds(Kb + off[c8], (lds_ptr_t)(uintptr_t)(kb_lds + 1024u * c8), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(Vb + off[c8], (lds_ptr_t)(uintptr_t)(vb_lds + 1024u * c8), 16, 0, 0);
     }
@@ -650,35 +683,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     // the SIMD's waves: the gather is bound by the bytes its waves keep in
     // flight
     __builtin_amdgcn_s_setprio(2);
-    u32x4 kf[8];
-    u32x2 vt[16];
-    read_chunk(ka, va, kf, vt);
+    u32x4 kf[4 * kSets];
+    u32x2 vt[8 * kSets];
+    if constexpr (kSets == 2) read_chunk(ka, va, kf, vt);
+    else read_chunk16(ka, va, kf, vt);
     if (ch + 1 < nch) {   // the buffers are free again: start the next chunk
       valid_next = rows_of(ch + 1, raw, off);
       issue(off);
       if (ch + 2 < nch) fetch_ids(ch + 2, raw);
     }
     __builtin_amdgcn_s_setprio(0);
-    f32x4 sc[2];
+    f32x4 sc[kSets];
 #pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
+    for (int sg = 0; sg < kSets; ++sg) {
       sc[sg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         sc[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[4 * sg + s]),
                                                          __builtin_bit_cast(bf16x8, qf[s]), sc[sg], 0, 0, 0);
     }
-    float x[8];   // index 4 sigma + r: token 16 sigma + 4q + r, head lane%G
+    constexpr int kE = 4 * kSets;   // logits per lane
+    float x[kE];   // index 4 sigma + r: token 16 sigma + 4q + r, head lane%G
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3];
+    for (int e = 0; e < kE; ++e) x[e] = sc[e >> 2][e & 3];
     if (valid != 0xffffffffu) {
       const unsigned vq = valid >> (4 * q);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < kE; ++e)
         if (!((vq >> ((e >> 2) * 16 + (e & 3))) & 1u)) x[e] = -INFINITY;
     }
-    float smax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    float smax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if constexpr (kSets == 2) smax = fmaxf(smax, fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     smax = max_xor<32>(max_xor<16>(smax));
     const float mnew = fmaxf(mrun, smax * c);
     if (__ballot(mnew != mrun)) {   // a head's maximum moved: rescale
@@ -695,14 +730,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
       }
       mrun = mnew;
     }
-    float p[8];
+    float p[kE];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[e], c, -mnew));
-    lrun += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    for (int e = 0; e < kE; ++e) p[e] = fast_exp2(fmaf(x[e], c, -mnew));
+    if constexpr (kSets == 2) lrun += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    else lrun += (p[0] + p[1]) + (p[2] + p[3]);
     // A operand: this lane's weights as bf16, hi or lo by its row
-    u32x4 pa;
+    unsigned pa[2 * kSets];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2 * kSets; ++j) {
       const unsigned hi =
           __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{p[2 * j], p[2 * j + 1]}, bf16x2));
       const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
@@ -711,9 +747,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sp
     }
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
-      const u32x4 vv = {vt[2 * bb].x, vt[2 * bb].y, vt[2 * bb + 1].x, vt[2 * bb + 1].y};
-      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                        __builtin_bit_cast(bf16x8, vv), acc[bb], 0, 0, 0);
+      if constexpr (kSets == 2) {
+        const u32x4 pv = {pa[0], pa[1], pa[2], pa[3]};
+        const u32x4 vv = {vt[2 * bb].x, vt[2 * bb].y, vt[2 * bb + 1].x, vt[2 * bb + 1].y};
+        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pv),
+                                                          __builtin_bit_cast(bf16x8, vv), acc[bb], 0, 0, 0);
+      } else {   // 16 tokens: k = 4q + r of the A operand is token 4q + r, as the value read gives it
+        const u32x2 pv = {pa[0], pa[1]};
+        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pv),
+                                                           __builtin_bit_cast(bf16x4, vt[bb]), acc[bb], 0, 0, 0);
+      }
     }
   }
   const float l = sum_xor<32>(sum_xor<16>(lrun));   // every lane: head lane%G
@@ -896,6 +939,13 @@ static hipError_t attn_by_e(const LayerShape& s, int key_block, int max_units, c
   return hipErrorInvalidValue;
 }
 
+// Tokens per chunk of the MFMA gather: key-block supports (contiguous runs
+// of rows, about 1024 keys a row) run 16-token chunks, which halve the LDS
+// per wave and let 16 waves share a CU; token supports keep 32-token chunks
+// (their rows' few hundred keys per key window would pay the per-chunk
+// bookkeeping twice as often).
+constexpr int kGatherTokensUnit = 32, kGatherTokensBlocks = 16;
+
 // One launch of the MFMA gather over rows >= n - rows (window w of nwin, or
 // the whole support when nwin = 0).
 static void launch_mfma_attn(const LayerShape& s, int key_block, int max_units, const void* q,
@@ -904,10 +954,11 @@ static void launch_mfma_attn(const LayerShape& s, int key_block, int max_units, 
                              const int32_t* starts, int nwin, int w, hipStream_t stream) {
   const int G = s.hq / s.hkv;
   const bool unit = key_block == 1;
-  auto kern = G == 1 ? (unit ? sparse_attn_mfma_kernel<true, 1> : sparse_attn_mfma_kernel<false, 1>)
-            : G == 2 ? (unit ? sparse_attn_mfma_kernel<true, 2> : sparse_attn_mfma_kernel<false, 2>)
-            : G == 4 ? (unit ? sparse_attn_mfma_kernel<true, 4> : sparse_attn_mfma_kernel<false, 4>)
-                     : (unit ? sparse_attn_mfma_kernel<true, 8> : sparse_attn_mfma_kernel<false, 8>);
+  constexpr int TU = kGatherTokensUnit, TB = kGatherTokensBlocks;
+  auto kern = G == 1 ? (unit ? sparse_attn_mfma_kernel<true, 1, TU> : sparse_attn_mfma_kernel<false, 1, TB>)
+            : G == 2 ? (unit ? sparse_attn_mfma_kernel<true, 2, TU> : sparse_attn_mfma_kernel<false, 2, TB>)
+            : G == 4 ? (unit ? sparse_attn_mfma_kernel<true, 4, TU> : sparse_attn_mfma_kernel<false, 4, TB>)
+                     : (unit ? sparse_attn_mfma_kernel<true, 8, TU> : sparse_attn_mfma_kernel<false, 8, TB>);
   int hkv_log2 = 0;
   while ((1 << hkv_log2) < s.hkv) ++hkv_log2;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * s.hkv)), dim3(64), 0, stream,

@@ -99,21 +99,25 @@ def test_key_tile_dma_and_operand_reads(d, elem):
 
 
 # ------------------------------------------------------------ the gather
-def test_gather_chunk_layout():
-    """sparse_attn_mfma_kernel: 32 tokens x 256 bytes of keys (values alike),
-    piece x of row R at position x ^ 2(R & 7); 16x16x32 operand reads."""
+@pytest.mark.parametrize("tok", [32, 16])
+def test_gather_chunk_layout(tok):
+    """sparse_attn_mfma_kernel: chunks of `tok` tokens (32: two sets of 16, for
+    token supports; 16: one set, for key blocks) x 256 bytes of keys (values
+    alike) in a buffer of tok * 256 bytes, piece x of row R at position
+    x ^ 2(R & 7); 16x16x32 key reads, value reads for 16x16x32 (two sets) or
+    16x16x16 (one set) products."""
     pos = {}
-    for c8 in range(8):
+    for c8 in range(tok // 4):
         for lane in range(64):
             q, m = lane >> 4, lane & 15
             xo = (m ^ (2 * q)) if c8 % 2 == 0 else (m ^ (8 + 2 * q))
             row, at = 4 * c8 + q, 1024 * c8 + 16 * lane
-            assert at + 16 <= 8192
+            assert at + 16 <= 256 * tok
             pos[(row, xo)] = at
             assert at == 256 * row + 16 * (xo ^ (2 * (row & 7)))
-    assert len(pos) == 32 * 16
+    assert len(pos) == tok * 16
     # key reads: lane (q, m) of set sigma, step s: row 16 sigma + m, d-chunk 4s + q
-    for sigma, s in itertools.product(range(2), range(4)):
+    for sigma, s in itertools.product(range(tok // 16), range(4)):
         addrs = []
         for lane in range(64):
             q, m = lane >> 4, lane & 15
@@ -124,7 +128,7 @@ def test_gather_chunk_layout():
         assert conflict_free(addrs, 16)
     # value reads (8 bytes each): lane 16q + 4e + b reads row 4q + e of a set,
     # d 16 blk + 4b + [0, 4), i.e. half (b & 1) of d-chunk 2 blk + b/2
-    for sigma, blk in itertools.product(range(2), range(8)):
+    for sigma, blk in itertools.product(range(tok // 16), range(8)):
         addrs = []
         for lane in range(64):
             q, e, b = lane >> 4, (lane >> 2) & 3, lane & 3
