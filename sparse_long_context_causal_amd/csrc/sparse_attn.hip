@@ -939,12 +939,12 @@ static hipError_t attn_by_e(const LayerShape& s, int key_block, int max_units, c
   return hipErrorInvalidValue;
 }
 
-// Tokens per chunk of the MFMA gather: key-block supports (contiguous runs
-// of rows, about 1024 keys a row) run 16-token chunks, which halve the LDS
-// per wave and let 16 waves share a CU; token supports keep 32-token chunks
-// (their rows' few hundred keys per key window would pay the per-chunk
-// bookkeeping twice as often).
-constexpr int kGatherTokensUnit = 32, kGatherTokensBlocks = 16;
+// Tokens per chunk of the MFMA gather: 16-token chunks halve the LDS per
+// wave and let 16 waves share a CU; key-block supports (contiguous runs of
+// rows) and short token supports run them, while token supports of more
+// than kShortSupport units keep 32-token chunks (their rows' few hundred
+// keys per key window would pay the per-chunk bookkeeping twice as often).
+constexpr int kShortSupport = 128;
 
 // One launch of the MFMA gather over rows >= n - rows (window w of nwin, or
 // the whole support when nwin = 0).
@@ -954,11 +954,13 @@ static void launch_mfma_attn(const LayerShape& s, int key_block, int max_units, 
                              const int32_t* starts, int nwin, int w, hipStream_t stream) {
   const int G = s.hq / s.hkv;
   const bool unit = key_block == 1;
-  constexpr int TU = kGatherTokensUnit, TB = kGatherTokensBlocks;
-  auto kern = G == 1 ? (unit ? sparse_attn_mfma_kernel<true, 1, TU> : sparse_attn_mfma_kernel<false, 1, TB>)
-            : G == 2 ? (unit ? sparse_attn_mfma_kernel<true, 2, TU> : sparse_attn_mfma_kernel<false, 2, TB>)
-            : G == 4 ? (unit ? sparse_attn_mfma_kernel<true, 4, TU> : sparse_attn_mfma_kernel<false, 4, TB>)
-                     : (unit ? sparse_attn_mfma_kernel<true, 8, TU> : sparse_attn_mfma_kernel<false, 8, TB>);
+  const bool t32 = unit && max_units > kShortSupport;
+#define AMTK_GATHER_KERNEL(GG)                                                          \
+  (t32 ? sparse_attn_mfma_kernel<true, GG, 32>                                          \
+       : unit ? sparse_attn_mfma_kernel<true, GG, 16> : sparse_attn_mfma_kernel<false, GG, 16>)
+  auto kern = G == 1 ? AMTK_GATHER_KERNEL(1) : G == 2 ? AMTK_GATHER_KERNEL(2)
+            : G == 4 ? AMTK_GATHER_KERNEL(4) : AMTK_GATHER_KERNEL(8);
+#undef AMTK_GATHER_KERNEL
   int hkv_log2 = 0;
   while ((1 << hkv_log2) < s.hkv) ++hkv_log2;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * s.hkv)), dim3(64), 0, stream,
