@@ -417,15 +417,35 @@ __device__ __forceinline__ void raise_bound_regs(const unsigned* words, int budg
   unsigned wv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) wv[j] = words[min(w0 + j, kFBinWords - 1)];
-  int b = bt;
-  int hb = 0;
-  while (true) {
-    const int j = (b >> 1) - w0;
-    const unsigned w = j == 0 ? wv[0] : j == 1 ? wv[1] : j == 2 ? wv[2] : j == 3 ? wv[3] : words[b >> 1];
-    hb = (int)((w >> ((b & 1) * 16)) & 0xffffu);
-    if (b >= kFBins - 1 || cg - hb < budget) break;
-    cg -= hb;
-    ++b;
+  // The walk moves from bin bt + t to bt + t + 1 while the candidates above
+  // it still number at least k: cg - S_t >= budget, S_t the counts of bins
+  // bt .. bt + t. S_t only grows, so the moves are a prefix and their number
+  // is the number of t that pass; the words in hand cover bins bt .. bt + 6
+  // (bt + 7 too when bt is even), so seven moves are counted without
+  // branches and a longer walk (rare) continues in the loop below.
+  const int odd = bt & 1;
+  int cnt[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) cnt[h] = (int)((wv[h >> 1] >> ((h & 1) * 16)) & 0xffffu);
+  int s = 0, sum = 0, moved = 0, hb = odd ? cnt[1] : cnt[0];
+#pragma unroll
+  for (int t = 0; t < 7; ++t) {
+    const int c = odd ? cnt[t + 1] : cnt[t];   // bin bt + t
+    sum += c;
+    const bool step = bt + t < kFBins - 1 && cg - sum >= budget;   // (a prefix of t)
+    s += step ? 1 : 0;
+    moved += step ? c : 0;
+    if (t < 6) hb = step ? (odd ? cnt[t + 2] : cnt[t + 1]) : hb;   // bin bt + s
+  }
+  cg -= moved;
+  int b = bt + s;
+  if (s == 7) {   // the walk goes on past the words in hand
+    while (true) {
+      hb = (int)((words[b >> 1] >> ((b & 1) * 16)) & 0xffffu);
+      if (b >= kFBins - 1 || cg - hb < budget) break;
+      cg -= hb;
+      ++b;
+    }
   }
   cge = cg;
   bt = b;
