@@ -736,26 +736,35 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       for (int e = 0; e < 4; ++e) pm[e] = sb[64 * e];
       const int pos0 = r_cnt;
       const unsigned thr = filter_bin_floor_bits(r_bt);
-      int pos = pos0;
-      const bool live = own_ok && pos <= cap;
-      int in_bt = 0;   // this tile's appends that fall in the bound's own bin
+      const bool live = own_ok && pos0 <= cap;
+      // the four keys' tests, ranks and bins first (independent of each
+      // other), then the pool stores and histogram adds: each under one flat
+      // condition, in key order
+      const int lim = diag ? own_q - k0 - own_j : 31;   // key 8e + own_j is causal iff 8e <= lim
+      bool fl[4];
+      unsigned long long mk[4];
+      int bn[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int mo = e * 8 + own_j;
-        const float p = pm[e];
-        const unsigned bits = __float_as_uint(p);
-        const int key = k0 + mo;
-        const bool flag = own_ok && bits >= thr && (!diag || key <= own_q);
-        const unsigned long long m = __ballot(flag) & grp_mask;
-        const int bin = filter_bin(p);
-        if (flag) {
-          const int at = pos + __popcll(m & below);
-          if (at < cap) cand[(size_t)own_q * cap + at] = make_uint2(bits, (unsigned)key);
-          if (live) lds_add(&own_hist[bin >> 1], 1u << ((bin & 1) * 16));
-        }
-        in_bt += __popcll(__ballot(flag && bin == r_bt) & grp_mask);
-        pos += __popcll(m);
+        fl[e] = own_ok && __float_as_uint(pm[e]) >= thr && 8 * e <= lim;
+        mk[e] = __ballot(fl[e]) & grp_mask;
+        bn[e] = filter_bin(pm[e]);
       }
+      int pos = pos0, in_bt = 0, at[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        at[e] = pos + __popcll(mk[e] & below);
+        pos += __popcll(mk[e]);
+        in_bt += __popcll(__ballot(fl[e] && bn[e] == r_bt) & grp_mask);
+      }
+      uint2* const row_pool = cand + (size_t)own_q * cap;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (fl[e] && at[e] < cap)
+          row_pool[at[e]] = make_uint2(__float_as_uint(pm[e]), (unsigned)(k0 + e * 8 + own_j));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (fl[e] && live) lds_add(&own_hist[bn[e] >> 1], 1u << ((bn[e] & 1) * 16));
       if (pos != pos0) {
         const int cg = r_cge + (pos - pos0);
         r_cnt = pos;
