@@ -407,6 +407,7 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; the other counters left at their maximum)
 constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }   // vmcnt(n), n < 64
 
 // A chunk's operands out of LDS: key fragment 4*sigma + s = 16-byte read at
 // ka[s] + 4096*sigma; value fragment 2*blk + sigma = transposing read at
@@ -664,20 +665,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ?
   }
   const float lo_sel = (m >= G && m < 2 * G) ? 1.0f : 0.0f;   // A-operand rows G..2G-1 carry lo
 
-  int raw[9];
+  // 32-token chunks: token ids run two chunks ahead, in two register sets
+  // taken in turn (the loop is unrolled by two). The set a chunk reads was
+  // filled before the previous chunk's wait, so the next chunk's load
+  // addresses are formed before this chunk's wait, and between the wait and
+  // the next chunk's loads there is only the copy out of LDS (1.3 % at 32K).
+  // 16-token chunks keep one set, one chunk ahead, and form the addresses
+  // after the copy: the second set and the early addresses would not fit
+  // their 128 registers.
+  constexpr bool kEarly = kTok == 32;
+  int rawA[9], rawB[9];
   unsigned off[8];
-  fetch_ids(0, raw);
-  unsigned valid_next = rows_of(0, raw, off);
+  fetch_ids(0, rawA);
+  unsigned valid_next = rows_of(0, rawA, off);
+  if (nch > 1) fetch_ids(1, rawA);
+  if (kEarly && nch > 2) fetch_ids(2, rawB);
   issue(off);
-  if (nch > 1) fetch_ids(1, raw);
+  if constexpr (kEarly) __builtin_amdgcn_s_waitcnt(vm_wait(2 * kDma));   // the ids of chunks 1 and 2
 
   f32x4 acc[8];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = kNegBig, lrun = 0.f;
-  for (int ch = 0; ch < nch; ++ch) {
+  auto chunk = [&](int ch, int (&r)[9]) __attribute__((always_inline)) {
     const unsigned valid = valid_next;
-    // every load in flight belongs to this chunk
+    // r holds the ids of chunk ch + 1 (kEarly: fetched two chunks back, so
+    // they have landed, and its load addresses are formed before the wait)
+    if (kEarly && ch + 1 < nch) valid_next = rows_of(ch + 1, r, off);
+    // every load in flight belongs to this chunk (and the ids of a later one)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // copying the chunk out and issuing the next one's loads go first among
     // the SIMD's waves: the gather is bound by the bytes its waves keep in
@@ -688,9 +703,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ?
     if constexpr (kSets == 2) read_chunk(ka, va, kf, vt);
     else read_chunk16(ka, va, kf, vt);
     if (ch + 1 < nch) {   // the buffers are free again: start the next chunk
-      valid_next = rows_of(ch + 1, raw, off);
-      issue(off);
-      if (ch + 2 < nch) fetch_ids(ch + 2, raw);
+      if constexpr (kEarly) {
+        issue(off);
+        if (ch + 3 < nch) fetch_ids(ch + 3, r);
+      } else {
+        valid_next = rows_of(ch + 1, r, off);
+        issue(off);
+        if (ch + 2 < nch) fetch_ids(ch + 2, r);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     f32x4 sc[kSets];
@@ -758,6 +778,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ?
                                                            __builtin_bit_cast(bf16x4, vt[bb]), acc[bb], 0, 0, 0);
       }
     }
+  };
+  if constexpr (kEarly) {
+    int ch = 0;
+    for (; ch + 1 < nch; ch += 2) {
+      chunk(ch, rawA);
+      chunk(ch + 1, rawB);
+    }
+    if (ch < nch) chunk(ch, rawA);
+  } else {
+    for (int ch = 0; ch < nch; ++ch) chunk(ch, rawA);
   }
   const float l = sum_xor<32>(sum_xor<16>(lrun));   // every lane: head lane%G
   const float inv = l > 0.f ? 1.0f / l : 0.f;
