@@ -274,16 +274,18 @@ def test_sparse_attn_one_token_and_empty(gpu_lib):
 
 
 @pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (8, 1), (64, 16), (16, 16)])
-@pytest.mark.parametrize("key_block", [1, 64])
-def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block, hq, hkv):
+@pytest.mark.parametrize("key_block,max_units", [(1, 48), (64, 48), (1, 200)])
+def test_sparse_attn_mfma_unsorted_invalid_and_clamped(gpu_lib, key_block, max_units, hq, hkv):
     """The MFMA path (bf16, d=128; 1, 2, 4 or 8 query heads per KV head) on
     hand-made supports: ids in random order (the running maximum moves late),
     negative ids and ids past the row mixed in, counts above max_units
     (clamped), empty rows. Every row is checked against the oracle on the ids
-    the contract keeps."""
+    the contract keeps. Token supports of up to 48 units take 16-token
+    chunks; 200 units take 32-token chunks (ids two chunks ahead), with every
+    chunk count from 0 to 7 among the rows."""
     import torch
     amtk = gpu_lib
-    n, max_units = 300, 48
+    n = 300
     rng = np.random.default_rng(77 + key_block)
     x = random_inputs(n, hq, hkv, 128, "bf16", seed=43 + hq + hkv, sink=True)
     layer = OracleLayer(x["q"], x["k"], x["v"])
