@@ -219,8 +219,11 @@ int sparse_attn_windowed_static(const amtk_attn_desc* attn, int32_t key_block,
  * tokens > i are skipped; a row left with no key gets O = 0 and LSE = -inf.
  * The result equals sparse_attn (same key_block) when every row of a block
  * holds the block's support.
- * Shapes: bf16, d = 128, hkv = 8, hq = 32, query_block = 64; anything else
- * returns AMTK_E_UNSUPPORTED (sparse_attn covers it row by row).
+ * query_block = 64. bf16, d = 128, hkv = 8, hq = 32 runs the block tile
+ * kernel (the block's keys gathered once); every other shape sparse_attn
+ * takes runs its per-row gather, each row reading its block's first index
+ * row (same result, keys gathered per row); anything else returns
+ * AMTK_E_UNSUPPORTED.
  *
  * idx       : [n][max_units] int32 (device); count: [n] int32 (device).
  * o         : OUT [n][hq][d] fp32.
@@ -284,7 +287,10 @@ int indexer_topk(int64_t n, int32_t d_idx, int32_t dtype, float scale,
  * sup->query_block = 64, key_block = 64: the fused realisation. After the
  * indexer's LSE pass one kernel per block of 64 queries scores the key
  * blocks, selects the shared top-k and attends over them for every KV head
- * (bf16, d = 128, hkv = 8, hq = 32, d_idx = 64, k <= 1024).
+ * (bf16, d = 128, hkv = 8, hq = 32, d_idx = 64, k <= 1024). With other
+ * backbone head layouts, or key_block = 1, the same support is formed by
+ * indexer_topk (query_block 64, written to every row of a block) and
+ * attended by sparse_attn row by row.
  * q_idx, k_idx: [n][d_idx], the layer's dtype. idx_scale <= 0: 1/sqrt(d_idx).
  * o: OUT [n][hq][d] fp32; idx/count/mass: OUT, the support as indexer_topk
  * writes it (mass may be NULL). ws: ws_bytes >= amtk_indexer_workspace(n,

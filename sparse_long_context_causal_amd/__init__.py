@@ -361,7 +361,8 @@ def indexer_prefill(q, k, v, q_idx, k_idx, budget: int, key_block: int = 64,
     """Indexer-driven sparse prefill: the indexer's support, then attention on
     it. query_block = 1: per query (indexer_topk + sparse_attn); 64: the fused
     realisation (one kernel per block of 64 queries scores, selects and
-    attends). Returns (out [N,Hq,d] fp32, idx, count, mass or None)."""
+    attends; other head layouts and token units: the block support, then the
+    per-row gather). Returns (out [N,Hq,d] fp32, idx, count, mass or None)."""
     torch = _torch()
     _check_dev(q, k, v, q_idx, k_idx)
     if v.shape != k.shape or v.dtype != k.dtype:

@@ -298,13 +298,20 @@ int sparse_attn_blocks(const amtk_attn_desc* attn, int32_t key_block, int32_t qu
   if (rc) return rc;
   if (max_units < 1) return AMTK_E_INVALID;
   if (key_block != 1 && key_block != 64) return AMTK_E_UNSUPPORTED;
-  if (!amtk::shared_attn_shape_supported(s, query_block)) return AMTK_E_UNSUPPORTED;
+  if (query_block != kQueryBlock) return AMTK_E_UNSUPPORTED;
+  // the block tile kernel where it covers the shape, else the per-row
+  // gather with every row reading its block's first index row
+  const bool tile = amtk::shared_attn_shape_supported(s, query_block);
+  if (!tile && !amtk::sparse_shape_supported(s)) return AMTK_E_UNSUPPORTED;
   if (!q || !k || !v || !idx || !count || !o) return AMTK_E_INVALID;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
       !aligned(count, 4) || !aligned(o, 16) || (lse_sparse && !aligned(lse_sparse, 4)))
     return AMTK_E_INVALID;
-  hipError_t e = amtk::launch_shared_attn(s, key_block, query_block, max_units, q, k, v, idx, count, o,
-                                          lse_sparse, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = tile ? amtk::launch_shared_attn(s, key_block, query_block, max_units, q, k, v, idx,
+                                                 count, o, lse_sparse, st)
+                      : amtk::launch_sparse_attn_block_rows(s, key_block, query_block, max_units, q,
+                                                            k, v, idx, count, o, lse_sparse, st);
   if (e != hipSuccess) return hip_fail(e);
   return AMTK_OK;
 }
@@ -489,10 +496,18 @@ int indexer_prefill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale,
     return e == hipSuccess ? AMTK_OK : hip_fail(e);
   }
   // fused realisation: the indexer's LSE pass, then one kernel per block of
-  // queries that scores, selects and attends
+  // queries that scores, selects and attends. Where that kernel does not
+  // cover the shapes (token units, other backbone head layouts), the same
+  // result in two steps: the block support (indexer_topk, written to
+  // every row of the block), then the per-row gather.
   if (sup->key_block == 1 || !amtk::shared_attn_shape_supported(s, sup->query_block) ||
-      !amtk::indexer_shared_supported(si.n, si.d, si.dtype, sup->key_block, sup->query_block, sup->k))
-    return AMTK_E_UNSUPPORTED;
+      !amtk::indexer_shared_supported(si.n, si.d, si.dtype, sup->key_block, sup->query_block, sup->k)) {
+    rc = run_topk(si, *sup, 0, q_idx, k_idx, idx, count, mass, nullptr, ws, ws_bytes, st);
+    if (rc) return rc;
+    hipError_t e = amtk::launch_sparse_attn(s, sup->key_block, sup->k, q, k, v, idx, count, o,
+                                            nullptr, st);
+    return e == hipSuccess ? AMTK_OK : hip_fail(e);
+  }
   if (!q_idx || !k_idx || !ws) return AMTK_E_INVALID;
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(ws, 256) || (mass && !aligned(mass, 4)))
     return AMTK_E_INVALID;

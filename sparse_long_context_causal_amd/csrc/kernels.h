@@ -77,6 +77,14 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
                               const void* k, const void* v, const int32_t* idx,
                               const int32_t* count, float* o, float* lse_sparse,
                               hipStream_t stream);
+// The same for selection blocks of query_block (a power of two) consecutive
+// rows: every row reads the ids and count of its block's first row and
+// skips the ids after itself. One pass, any shape sparse_attn takes.
+hipError_t launch_sparse_attn_block_rows(const LayerShape& s, int key_block, int query_block,
+                                         int max_units, const void* q, const void* k,
+                                         const void* v, const int32_t* idx,
+                                         const int32_t* count, float* o, float* lse_sparse,
+                                         hipStream_t stream);
 // The same in key windows (one launch per window, partial softmax merged
 // into o); scratch of sparse_windowed_scratch_bytes. Falls back to
 // launch_sparse_attn where the windowed form does not apply.

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
     float* __restrict__ lse_out, int n, int hkv, int D, int key_block, int max_units, float c,
-    float tau) {
+    float tau, int qb_log2) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = n - 1 - (int)(blockIdx.x * kAttnWaves + wave);
   if (i < 0) return;
@@ -106,9 +106,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     m[h] = kNegBig;
     l[h] = 0.f;
   }
-  const int cnt = min(max(count[i], 0), max_units);
+  const int srow = (i >> qb_log2) << qb_log2;   // the row that holds row i's support
+  const int cnt = min(max(count[srow], 0), max_units);
   const int total = cnt * key_block;
-  const int32_t* ids = idx + (size_t)i * max_units;
+  const int32_t* ids = idx + (size_t)srow * max_units;
   const size_t off = (size_t)g * D + e0;
 
   for (int t0 = 0; t0 < total; t0 += CH) {
@@ -228,7 +229,7 @@ template <int CH>
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
-    float* __restrict__ lse_out, int n, int key_block, int max_units, float c) {
+    float* __restrict__ lse_out, int n, int key_block, int max_units, float c, int qb_log2) {
   constexpr int D = 128, HKV = 8, G = 4, E = 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = n - 1 - (int)(blockIdx.x * kAttnWaves + wave);
@@ -254,9 +255,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
     for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
   float m = kNegBig, l = 0.f;   // softmax state of head myh
 
-  const int cnt = min(max(count[i], 0), max_units);
+  const int srow = (i >> qb_log2) << qb_log2;   // the row that holds row i's support
+  const int cnt = min(max(count[srow], 0), max_units);
   const int total = cnt * key_block;
-  const int32_t* ids = idx + (size_t)i * max_units;
+  const int32_t* ids = idx + (size_t)srow * max_units;
 
   for (int t0 = 0; t0 < total; t0 += CH) {
     int jj[CH];
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ?
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ O,
     float* __restrict__ lse_out, int n, int hkv_log2, int key_block, int max_units, float c,
-    const int32_t* __restrict__ wstart, int nwin, int win) {
+    const int32_t* __restrict__ wstart, int nwin, int win, int qb_log2) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per KV head");
   constexpr int D = 128;
   const int hkv = 1 << hkv_log2;   // a power of two: rows and heads by shifts
@@ -536,7 +538,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ?
   const int i = n - 1 - (int)(blockIdx.x >> hkv_log2);   // longest rows first
   const int g = (int)(blockIdx.x & (unsigned)(hkv - 1));
   const int m = lane & 15, q = lane >> 4;
-  int cnt = min(max(count[i], 0), max_units);
+  // row i's support: its own index row, or with selection blocks of
+  // 2^qb_log2 queries (one pass only) the block's first row
+  const int srow = (i >> qb_log2) << qb_log2;
+  int cnt = min(max(count[srow], 0), max_units);
   // Key windows (nwin > 0): this launch takes the support's units that lie
   // in window win, positions wstart[win] .. wstart[win + 1] of the row, and
   // merges its partial softmax with the earlier windows' (O normalised,
@@ -562,7 +567,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kTok == 16 ?
     if (lse_out && lane < G) lse_out[(size_t)(G * g + lane) * n + i] = -INFINITY;
     return;
   }
-  const int32_t* ids = idx + (size_t)i * max_units + s0;
+  const int32_t* ids = idx + (size_t)srow * max_units + s0;
   unsigned char* kbuf = smem;
   unsigned char* vbuf = smem + kBuf;
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K) + g * (D * 2);
@@ -902,13 +907,14 @@ __global__ __launch_bounds__(256) void support_windows_kernel(
 template <typename T, int E, int G>
 static hipError_t run_attn(const LayerShape& s, int key_block, int max_units, const void* q,
                            const void* k, const void* v, const int32_t* idx,
-                           const int32_t* count, float* o, float* lse, hipStream_t stream) {
+                           const int32_t* count, float* o, float* lse, int qb_log2,
+                           hipStream_t stream) {
   constexpr int CH = (E >= 16) ? 4 : 8;
   const int blocks = (s.n + kAttnWaves - 1) / kAttnWaves;
   hipLaunchKernelGGL((sparse_attn_kernel<T, E, G, CH>), dim3(blocks), dim3(64 * kAttnWaves), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), idx, count, o, lse, s.n, s.hkv, s.d, key_block,
-                     max_units, s.scale * kLog2e, s.scale);
+                     max_units, s.scale * kLog2e, s.scale, qb_log2);
   return hipGetLastError();
 }
 
@@ -944,28 +950,36 @@ bool sparse_shape_supported(const LayerShape& s) {
 template <typename T, int E>
 static hipError_t attn_by_g(const LayerShape& s, int key_block, int max_units, const void* q,
                             const void* k, const void* v, const int32_t* idx,
-                            const int32_t* count, float* o, float* lse, hipStream_t stream) {
+                            const int32_t* count, float* o, float* lse, int qb_log2,
+                            hipStream_t stream) {
   const int G = s.hq / s.hkv;
+#define AMTK_RUN_ATTN(GG) \
+  run_attn<T, E, GG>(s, key_block, max_units, q, k, v, idx, count, o, lse, qb_log2, stream)
   if constexpr (E <= 8) {
-    if (G == 8) return run_attn<T, E, 8>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
+    if (G == 8) return AMTK_RUN_ATTN(8);
   }
-  if (G == 1) return run_attn<T, E, 1>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
-  if (G == 2) return run_attn<T, E, 2>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
-  if (G == 4) return run_attn<T, E, 4>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
+  if (G == 1) return AMTK_RUN_ATTN(1);
+  if (G == 2) return AMTK_RUN_ATTN(2);
+  if (G == 4) return AMTK_RUN_ATTN(4);
+#undef AMTK_RUN_ATTN
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t attn_by_e(const LayerShape& s, int key_block, int max_units, const void* q,
                             const void* k, const void* v, const int32_t* idx,
-                            const int32_t* count, float* o, float* lse, hipStream_t stream) {
+                            const int32_t* count, float* o, float* lse, int qb_log2,
+                            hipStream_t stream) {
+#define AMTK_ATTN_E(EE) \
+  attn_by_g<T, EE>(s, key_block, max_units, q, k, v, idx, count, o, lse, qb_log2, stream)
   switch (slice_width(s)) {
-    case 1: return attn_by_g<T, 1>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
-    case 2: return attn_by_g<T, 2>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
-    case 4: return attn_by_g<T, 4>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
-    case 8: return attn_by_g<T, 8>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
-    case 16: return attn_by_g<T, 16>(s, key_block, max_units, q, k, v, idx, count, o, lse, stream);
+    case 1: return AMTK_ATTN_E(1);
+    case 2: return AMTK_ATTN_E(2);
+    case 4: return AMTK_ATTN_E(4);
+    case 8: return AMTK_ATTN_E(8);
+    case 16: return AMTK_ATTN_E(16);
   }
+#undef AMTK_ATTN_E
   return hipErrorInvalidValue;
 }
 
@@ -981,7 +995,8 @@ constexpr int kShortSupport = 128;
 static void launch_mfma_attn(const LayerShape& s, int key_block, int max_units, const void* q,
                              const void* k, const void* v, const int32_t* idx,
                              const int32_t* count, float* o, float* lse, long long rows,
-                             const int32_t* starts, int nwin, int w, hipStream_t stream) {
+                             const int32_t* starts, int nwin, int w, hipStream_t stream,
+                             int qb_log2 = 0) {
   const int G = s.hq / s.hkv;
   const bool unit = key_block == 1;
   const bool t32 = unit && max_units > kShortSupport;
@@ -996,16 +1011,17 @@ static void launch_mfma_attn(const LayerShape& s, int key_block, int max_units, 
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * s.hkv)), dim3(64), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), idx, count, o, lse, s.n, hkv_log2, key_block,
-                     max_units, s.scale * kLog2e, starts, nwin, w);
+                     max_units, s.scale * kLog2e, starts, nwin, w, qb_log2);
 }
 
-hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units, const void* q,
-                              const void* k, const void* v, const int32_t* idx,
-                              const int32_t* count, float* o, float* lse_sparse,
-                              hipStream_t stream) {
+// One pass of the gather; row i reads the support of row (i >> qb_log2) << qb_log2.
+static hipError_t sparse_attn_rows(const LayerShape& s, int key_block, int max_units,
+                                   const void* q, const void* k, const void* v,
+                                   const int32_t* idx, const int32_t* count, float* o,
+                                   float* lse_sparse, int qb_log2, hipStream_t stream) {
   if (mfma_attn_shape(s, key_block)) {
     launch_mfma_attn(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, s.n, nullptr, 0,
-                     0, stream);
+                     0, stream, qb_log2);
     return hipGetLastError();
   }
   if (s.dtype == kBF16 && s.d == 128 && s.hkv == 8 && s.hq == 32) {
@@ -1014,12 +1030,33 @@ hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units,
     hipLaunchKernelGGL((sparse_attn_g4_kernel<CH>), dim3(blocks), dim3(64 * kAttnWaves), 0, stream,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                        static_cast<const bf16_t*>(v), idx, count, o, lse_sparse, s.n, key_block,
-                       max_units, s.scale * kLog2e);
+                       max_units, s.scale * kLog2e, qb_log2);
     return hipGetLastError();
   }
   if (s.dtype == kBF16)
-    return attn_by_e<bf16_t>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
-  return attn_by_e<float>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, stream);
+    return attn_by_e<bf16_t>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, qb_log2,
+                             stream);
+  return attn_by_e<float>(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, qb_log2,
+                          stream);
+}
+
+hipError_t launch_sparse_attn(const LayerShape& s, int key_block, int max_units, const void* q,
+                              const void* k, const void* v, const int32_t* idx,
+                              const int32_t* count, float* o, float* lse_sparse,
+                              hipStream_t stream) {
+  return sparse_attn_rows(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, 0, stream);
+}
+
+hipError_t launch_sparse_attn_block_rows(const LayerShape& s, int key_block, int query_block,
+                                         int max_units, const void* q, const void* k,
+                                         const void* v, const int32_t* idx,
+                                         const int32_t* count, float* o, float* lse_sparse,
+                                         hipStream_t stream) {
+  if (query_block < 1 || (query_block & (query_block - 1))) return hipErrorInvalidValue;
+  int qb_log2 = 0;
+  while ((1 << qb_log2) < query_block) ++qb_log2;
+  return sparse_attn_rows(s, key_block, max_units, q, k, v, idx, count, o, lse_sparse, qb_log2,
+                          stream);
 }
 
 // ------------------------------------------------------- windowed gather

@@ -172,9 +172,13 @@ def test_sparse_attn_blocks_validation(lib):
     f = lib.sparse_attn_blocks
     a, _ = _descs()
     assert f(ctypes.byref(a), 1, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
-    # the tile kernel's shape only: bf16, d = 128, 8 KV x 4 query heads, blocks of 64
-    assert f(ctypes.byref(a), 1, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    # head layouts other than the tile kernel's (fp32 8/2 here) run the per-row
+    # gather on the blocks' first rows: the shape passes, the null v fails
+    assert f(ctypes.byref(a), 1, 64, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(ctypes.byref(a), 64, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
     from sparse_long_context_causal_amd import _abi
+    g3 = _abi.AttnDesc(1000, 24, 8, 128, _abi.AMTK_BF16, 1, 0.0)   # 3 query heads per KV head
+    assert f(ctypes.byref(g3), 1, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
     b = _abi.AttnDesc(1000, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
     assert f(ctypes.byref(b), 1, 32, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
     assert f(ctypes.byref(b), 16, 64, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
@@ -197,11 +201,15 @@ def test_indexer_prefill_validation(lib):
                             *kw.get("args", args), *kw.get("outs", outs), FAKE,
                             kw.get("ws", need.value), None)
     assert ok(s_fused, ws=need.value - 1) == -3
-    assert ok(s_fused, di=32) == -2                     # the fused kernel wants d_idx = 64
-    assert ok(_abi.SupportDesc(16, 1, 64, 0)) == -2     # fused: key blocks of 64 only
-    assert ok(_abi.SupportDesc(2000, 64, 64, 0)) == -2  # more winners than its LDS holds
+    assert ok(s_fused, di=32) == -2                     # indexer heads of 64 or 128 only
+    # token units: the indexer's column-sum top-k, then the per-row gather
+    # (stopped here by its workspace check, before any launch)
+    assert ok(_abi.SupportDesc(16, 1, 64, 0), ws=0) == -3
+    assert ok(_abi.SupportDesc(2000, 64, 64, 0)) == -2  # more winners than the block kernel's LDS holds
     a, _ = _descs()
-    assert ok(s_fused, a=a) == -2                       # not the tile kernel's layer shape
+    assert ok(s_fused, a=a, ws=0) == -3                 # other layouts: the two-step realisation
+    g3 = _abi.AttnDesc(1000, 24, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    assert ok(s_fused, a=g3) == -2                      # a layout no gather takes
     assert ok(s_fused, outs=[None, FAKE, FAKE, None]) == -1
     assert ok(s_fused, args=[FAKE, FAKE, FAKE, None, FAKE]) == -1
     # the per-query realisation checks the backbone q and k before any launch

@@ -32,11 +32,11 @@ def _t(a):
     return torch.from_numpy(a).to(torch.bfloat16).cuda()
 
 
-def _check_blocks(idx, cnt, mass, ix, n, k, blocks=None):
+def _check_blocks(idx, cnt, mass, ix, n, k, blocks=None, key_block=64):
     nblk = (n + 63) // 64
     res = {}
     for t in (range(nblk) if blocks is None else blocks):
-        r = ix.query_block(int(t), k, 64, 64)
+        r = ix.query_block(int(t), k, key_block, 64)
         rows = list(r["rows"])
         i0 = rows[0]
         for i in rows:
@@ -152,3 +152,41 @@ def test_indexer_prefill_fused_indexer_bf16_32k_sampled(gpu_lib):
             o_ref, _ = layer.attention_on(i, toks)
             err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
             assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
+
+
+@pytest.mark.parametrize("hq,hkv,kb,k", [
+    (16, 2, 64, 4),     # 8 query heads per KV head, key blocks
+    (8, 8, 64, 3),      # one query head per KV head
+    (32, 8, 1, 100),    # the tile kernel's layout, but token units
+])
+def test_indexer_prefill_blocks_two_step(gpu_lib, hq, hkv, kb, k):
+    """indexer_prefill with selection blocks where the fused kernel does not
+    apply: the block support (as indexer_topk writes it), then the per-row
+    gather. Bit for bit against those two calls; the supports against the
+    oracle's block scores, the outputs against its attention on the shared
+    tokens up to each row."""
+    import torch
+    amtk = gpu_lib
+    n = 330
+    x = random_inputs(n, hq, hkv, 128, "bf16", seed=hq + hkv + kb, sink=True)
+    qi, ki = _idx_inputs(n, hq * 3 + kb)
+    d = upload(x, "bf16")
+    tq, tk = _t(qi), _t(ki)
+    out_f, idx_f, cnt_f, mass_f = amtk.indexer_prefill(d["q"], d["k"], d["v"], tq, tk, k, kb,
+                                                       query_block=64)
+    idx_u, cnt_u, mass_u = amtk.indexer_topk(tq, tk, k, kb, query_block=64)
+    out_u, _ = amtk.sparse_attn(d["q"], d["k"], d["v"], idx_u, cnt_u, kb)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx_u) and torch.equal(cnt_f, cnt_u) and torch.equal(mass_f, mass_u)
+    assert torch.equal(out_f, out_u)
+    ix = IndexerOracle(qi, ki)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    ii, cc = idx_f.cpu().numpy(), cnt_f.cpu().numpy()
+    _check_blocks(ii, cc, mass_f.cpu().numpy(), ix, n, k, key_block=kb)
+    out = out_f.cpu().numpy()
+    for i in range(0, n, 7):
+        units = ii[i, : cc[i]]
+        toks = tokens_of_blocks(units, kb, i) if kb > 1 else units[units <= i]
+        o_ref, _ = layer.attention_on(i, toks)
+        err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
+        assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"

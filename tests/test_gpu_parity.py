@@ -81,6 +81,27 @@ def test_budget_at_least_row_length_is_dense(gpu_lib):
         assert np.max(np.abs(res["out"][i] - layer.dense(i))) <= TOL_OUT["bf16"]
 
 
+@pytest.mark.parametrize("n,hq,hkv,d,dtype", [
+    (9000, 32, 8, 128, "bf16"),   # MFMA passes with direct key tiles, windowed MFMA gather (2 windows)
+    (8300, 8, 2, 64, "f32"),      # fp32 passes, VALU gather
+])
+def test_largest_budget(gpu_lib, n, hq, hkv, d, dtype):
+    """The largest budget the select sorts (k = 8192 tokens): rows up to
+    8191 keep every visible key, later rows the exact top 8192 of up to
+    9000, which the select's LDS cannot stage (global-memory radix path)."""
+    k = 8192                      # the header's upper limit of k
+    x = random_inputs(n, hq, hkv, d, dtype, seed=n + hq, sink=True)
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([[0, 1, 31, k - 2, k - 1, k, k + 1, n - 2, n - 1],
+                                     rng.integers(k, n, 5), rng.integers(0, k, 3)]))
+    res, _ = _full_check(gpu_lib, x, dtype, k, rows=rows)
+    for i in rows:
+        assert res["count"][i] == min(i + 1, k)
+        if i < k:
+            assert res["idx"][i][: i + 1].tolist() == list(range(i + 1))
+            assert np.all(res["idx"][i][i + 1:] == -1)
+
+
 @pytest.mark.parametrize("n", [120, 3000])   # 3000: rows keep more than the select's LDS holds
 def test_equal_keys_tie_to_smallest_ids(gpu_lib, n):
     hq, hkv, d = 8, 2, 64
@@ -410,6 +431,53 @@ def test_sparse_attn_blocks_oracle_supports(gpu_lib):
             assert np.all(np.isneginf(lse[:, i])), f"row {i} lse"
         else:
             assert np.max(np.abs(lse[:, i] - r["lse_s"][i])) <= TOL_LSE["bf16"], f"row {i} lse"
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [
+    (16, 2, 128, "bf16"),   # MFMA gather, 8 query heads per KV head
+    (8, 8, 128, "bf16"),    # MFMA gather, one query head per KV head
+    (8, 2, 64, "f32"),      # VALU gather
+])
+def test_sparse_attn_blocks_other_layouts(gpu_lib, hq, hkv, d, dtype):
+    """Head layouts outside the block tile kernel run the per-row gather, each
+    row reading its block's first index row (the other rows hold junk): every
+    row against the oracle's block outputs and support LSE, and bit for bit
+    against sparse_attn on per-row copies of the block supports."""
+    import torch
+    amtk = gpu_lib
+    n, k = 330, 40                      # 6 blocks, the last with 10 rows
+    x = random_inputs(n, hq, hkv, d, dtype, seed=hq * 10 + hkv, sink=True)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    idx = np.full((n, k), -5, dtype=np.int32)
+    cnt = np.full(n, 7, dtype=np.int32)
+    per_idx = np.full((n, k), -1, dtype=np.int32)
+    per_cnt = np.zeros(n, dtype=np.int32)
+    res = {}
+    for t in range((n + 63) // 64):
+        r = layer.query_block(t, k, 64)
+        res[t] = r
+        u = r["units"]
+        idx[64 * t, :] = -1
+        idx[64 * t, : u.size] = u
+        cnt[64 * t] = u.size
+        per_idx[64 * t: 64 * t + 64] = idx[64 * t]
+        per_cnt[64 * t: 64 * t + 64] = u.size
+    dv = upload(x, dtype)
+    out, lse = amtk.sparse_attn_blocks(dv["q"], dv["k"], dv["v"], torch.from_numpy(idx).cuda(),
+                                       torch.from_numpy(cnt).cuda(), 64, want_lse=True)
+    out_r, lse_r = amtk.sparse_attn(dv["q"], dv["k"], dv["v"], torch.from_numpy(per_idx).cuda(),
+                                    torch.from_numpy(per_cnt).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_r) and torch.equal(lse, lse_r)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in range(n):
+        r = res[i // 64]
+        err = float(np.max(np.abs(out[i].astype(np.float64) - r["out"][i])))
+        assert err <= TOL_OUT[dtype], f"row {i}: max abs err {err}"
+        if np.all(np.isneginf(r["lse_s"][i])):
+            assert np.all(np.isneginf(lse[:, i])), f"row {i} lse"
+        else:
+            assert np.max(np.abs(lse[:, i] - r["lse_s"][i])) <= TOL_LSE[dtype], f"row {i} lse"
 
 
 def test_sparse_attn_blocks_unsorted_invalid_and_clamped(gpu_lib):
