@@ -190,3 +190,47 @@ def test_indexer_prefill_blocks_two_step(gpu_lib, hq, hkv, kb, k):
         o_ref, _ = layer.attention_on(i, toks)
         err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
         assert err <= TOL_OUT["bf16"], f"row {i}: max abs err {err}"
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [
+    (16, 2, 128, "bf16"),   # MFMA gather over key blocks, 8 query heads per KV head
+    (8, 2, 64, "f32"),      # VALU gather
+])
+def test_sparse_attn_blocks_key_blocks_other_layouts(gpu_lib, hq, hkv, d, dtype):
+    """sparse_attn_blocks over 64-token key blocks on layouts outside the tile
+    kernel (the per-row gather reading each block's first index row), driven by
+    the oracle's indexer supports: every row against the oracle's attention on
+    the block's tokens up to the row, and bit for bit against sparse_attn on
+    per-row copies."""
+    import torch
+    n, k = 300, 3
+    x = random_inputs(n, hq, hkv, d, dtype, seed=53 + hq, sink=True)
+    qi, ki = _idx_inputs(n, 54)
+    ix = IndexerOracle(qi, ki)
+    layer = OracleLayer(x["q"], x["k"], x["v"])
+    idx = np.full((n, k), -3, dtype=np.int32)
+    cnt = np.full(n, 1, dtype=np.int32)
+    per_idx = np.full((n, k), -1, dtype=np.int32)
+    per_cnt = np.zeros(n, dtype=np.int32)
+    units = {}
+    for t in range((n + 63) // 64):
+        u = ix.query_block(t, k, 64, 64)["units"]
+        units[t] = u
+        idx[64 * t] = -1
+        idx[64 * t, : u.size] = u
+        cnt[64 * t] = u.size
+        per_idx[64 * t: 64 * t + 64] = idx[64 * t]
+        per_cnt[64 * t: 64 * t + 64] = u.size
+    dv = upload(x, dtype)
+    out, lse = gpu_lib.sparse_attn_blocks(dv["q"], dv["k"], dv["v"], torch.from_numpy(idx).cuda(),
+                                          torch.from_numpy(cnt).cuda(), 64, key_block=64,
+                                          want_lse=True)
+    out_r, lse_r = gpu_lib.sparse_attn(dv["q"], dv["k"], dv["v"], torch.from_numpy(per_idx).cuda(),
+                                       torch.from_numpy(per_cnt).cuda(), 64, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_r) and torch.equal(lse, lse_r)
+    out = out.cpu().numpy()
+    for i in range(n):
+        o_ref, _ = layer.attention_on(i, tokens_of_blocks(units[i // 64], 64, i))
+        err = float(np.max(np.abs(out[i].astype(np.float64) - o_ref)))
+        assert err <= TOL_OUT[dtype], f"row {i}: max abs err {err}"
