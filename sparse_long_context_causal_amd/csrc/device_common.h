@@ -173,6 +173,24 @@ __device__ __forceinline__ void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2,
       : "memory");
 }
 
+// The same for 8 chunks: one round trip instead of two.
+__device__ __forceinline__ void lds_read8(const uint32_t (&a)[8], uint4 (&x)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Per-lane constants of the key-tile layout for one launch, two VGPRs.
 // The swizzle only flips address bits that the row and slot bases leave
 // clear, so every offset is one of these XOR a compile-time constant:
@@ -221,10 +239,17 @@ struct KLane {
   // tile in `slot`.
   __device__ __forceinline__ void read(const unsigned char* slot, uint4 (&kc)[L::kNc]) const {
     const uint32_t a = lds_addr(slot) + rx;
+    if constexpr (L::kNc == 8) {   // one round trip for the whole operand
+      uint32_t ad[8];
 #pragma unroll
-    for (int k = 0; k < L::kNc; k += 4)
-      lds_read4(a ^ (16u * k), a ^ (16u * (k + 1)), a ^ (16u * (k + 2)), a ^ (16u * (k + 3)),
-                kc[k], kc[k + 1], kc[k + 2], kc[k + 3]);
+      for (int k = 0; k < 8; ++k) ad[k] = a ^ (16u * k);
+      lds_read8(ad, kc);
+    } else {
+#pragma unroll
+      for (int k = 0; k < L::kNc; k += 4)
+        lds_read4(a ^ (16u * k), a ^ (16u * (k + 1)), a ^ (16u * (k + 2)), a ^ (16u * (k + 3)),
+                  kc[k], kc[k + 1], kc[k + 2], kc[k + 3]);
+    }
   }
 };
 
