@@ -706,21 +706,20 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
       const uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane(
           (int)(part_lds + (uint32_t)((ft & 1) * part_floats * 4)));
       float* sb = sums + (ft & 1) * 1024 + ow * 256 + lane;
+      // the four keys' partials in one round trip
+      const uint32_t ad[4] = {pb + hs_off[0], pb + hs_off[1], pb + hs_off[2], pb + hs_off[3]};
+      f32x2 v[16];
+      read_partials_hk8x4(ad, v);
 #pragma unroll
-      for (int e2 = 0; e2 < 4; e2 += 2) {   // two keys per round trip
-        f32x2 v[8];
-        read_partials_hk8(pb + hs_off[e2], pb + hs_off[e2 + 1], v);
+      for (int e = 0; e < 4; ++e) {
+        float p = v[4 * e].x;
+        p += v[4 * e].y;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float p = v[4 * u].x;
-          p += v[4 * u].y;
-#pragma unroll
-          for (int j = 1; j < 4; ++j) {
-            p += v[4 * u + j].x;
-            p += v[4 * u + j].y;
-          }
-          sb[64 * (e2 + u)] = p * inv_hq;
+        for (int j = 1; j < 4; ++j) {
+          p += v[4 * e + j].x;
+          p += v[4 * e + j].y;
         }
+        sb[64 * e] = p * inv_hq;
       }
     };
     // the owner's filter of tile ft (see the generic loop below)
