@@ -346,16 +346,18 @@ int amtk_kl_workspace(const amtk_attn_desc* attn, int32_t d_idx, size_t* bytes);
  *   dq_idx[i] = dloss/dq_idx[i] = (idx_scale/n) sum_j (Q_ij - P_ij) k_idx[j]
  *   dk_idx[j] = dloss/dk_idx[j] = (idx_scale/n) sum_{i>=j} (Q_ij - P_ij) q_idx[i]
  * No n x n matrix, and no array of that size, is stored: the workspace is
- * O(n * (hq + 8 * d_idx)) floats (the dense LSE, the student LSE and the key
- * gradient's per-KV-group shares). Both gradients are deterministic (fixed
- * summation order).
- * q, k      : as for topk_support; bf16, d = 128, hkv = 8, hq = 32 only.
+ * O(n * (hq + hkv * d_idx)) floats (the dense LSE, the student LSE and the
+ * key gradient's per-KV-group shares). Both gradients are deterministic
+ * (fixed summation order).
+ * q, k      : as for topk_support; bf16, d = 128, 4 query heads per KV head
+ *             and 1, 2, 4 or 8 KV heads (hq = 4 * hkv); anything else returns
+ *             AMTK_E_UNSUPPORTED.
  * q_idx     : [n][d_idx] bf16 (device), k_idx: [n][d_idx] bf16; d_idx = 64.
  * kl_row    : OUT [n] fp32.   loss: OUT [1] fp32, or NULL.
  * dq_idx    : OUT [n][d_idx] fp32.   dk_idx: OUT [n][d_idx] fp32.
  * ws        : device workspace of ws_bytes >= amtk_kl_workspace()
- *             (n * (hq + 1 + 8 * d_idx) * 4 bytes plus alignment: 71 MB at
- *             n = 32768).
+ *             (n * (hq + 1 + hkv * d_idx) * 4 bytes plus alignment: 71 MB at
+ *             n = 32768 with 32/8 heads).
  */
 int kl_distill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale, const void* q,
                const void* k, const void* q_idx, const void* k_idx, float* kl_row, float* loss,

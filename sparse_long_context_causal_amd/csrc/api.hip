@@ -411,7 +411,7 @@ KlLayout kl_layout(const LayerShape& s) {
   L.lse = off;    off = round_up(off + (size_t)s.hq * s.n * sizeof(float));
   L.lse_t = off;  off = round_up(off + (size_t)s.n * sizeof(float));
   L.zero = off;   off = round_up(off + sizeof(int));
-  L.part = off;   off = round_up(off + amtk::kl_partial_bytes(s.n));
+  L.part = off;   off = round_up(off + amtk::kl_partial_bytes(s.n, s.hkv));
   L.total = off;
   return L;
 }

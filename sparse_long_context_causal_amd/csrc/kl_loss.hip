@@ -14,11 +14,12 @@
 // Both log-sum-exps come first from pass 1 (teacher per head, student with
 // one head of d_idx).
 //
-// kl_tile_kernel (bf16, d = 128, 8 KV heads x 4 query heads, d_idx = 64),
-// query-major: one workgroup of 8 waves per 32-query tile, wave g = KV head
-// g, key tiles streamed as in pass 2. Per key tile:
-//  * every wave scores its 4 heads (32x32x16 MFMAs), turns them into
-//    probabilities with the dense LSE and sums them; the 8 partial tiles
+// kl_tile_kernel (bf16, d = 128, 4 query heads per KV head, 1, 2, 4 or 8 KV
+// heads, d_idx = 64), query-major: one workgroup of 8 waves per 32-query
+// tile, wave g < hkv = KV head g, key tiles streamed as in pass 2. Per key
+// tile:
+//  * every wave g < hkv scores its 4 heads (32x32x16 MFMAs), turns them into
+//    probabilities with the dense LSE and sums them; the hkv partial tiles
 //    meet in LDS and the workgroup assembles the teacher tile P[key][query];
 //  * waves 0 and 1 compute the student tile t^T[key][query] (4 MFMAs),
 //    Q and dS = Q - P in the score layout (lane = query), the KL terms of
@@ -43,6 +44,7 @@ namespace amtk {
 
 namespace {
 
+// kKlHkv, kKlHq: the most KV / query heads (the LDS map is sized for them)
 constexpr int kKlD = 128, kKlG = 4, kKlHkv = 8, kKlHq = kKlHkv * kKlG, kKlDi = 64;
 typedef KTile<bf16_t, kKlD> KlKT;
 constexpr int kKlNc = KlKT::kChunks;
@@ -139,15 +141,19 @@ __device__ __forceinline__ void dq_store(uint32_t a, const f32x16& acc) {
       : "memory");
 }
 
+template <int HKV>
 __global__ __launch_bounds__(512) void kl_tile_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ QI,
     const bf16_t* __restrict__ KI, const float* __restrict__ lse, const float* __restrict__ lse_t,
-    int n, float c, float ct, float* __restrict__ kl_row, float* __restrict__ dq,
-    float grad_scale) {
+    int n, float inv_hq, float c, float ct, float* __restrict__ kl_row,
+    float* __restrict__ dq, float grad_scale) {
+  constexpr int hkv = HKV;
   extern __shared__ __align__(1024) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
   const int g = wave;
+  const bool teacher = g < hkv;   // (uniform per wave) KV head g exists
+  const int hq = kKlG * hkv;
   const int ntiles = (n + 31) >> 5;
   const int qt = ntiles - 1 - (int)blockIdx.x;   // longest rows first
   const int q0 = qt << 5;
@@ -158,8 +164,8 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
   unsigned char* slot = smem + kKlSlots + wave * KlKT::kBytes;
 
   KLane<bf16_t, kKlD> kl;
-  kl.init(lane, kKlHkv);
-  kl.issue(K, n, kKlHkv, g, 0, slot);
+  kl.init(lane, hkv);
+  if (teacher) kl.issue(K, n, hkv, g, 0, slot);
   // k_idx tile kt, rows 8w .. 8w+7 by wave w < 4 (lane: row 8w + lane/8,
   // position lane%8, holding d-chunk (lane%8) ^ f(row))
   const unsigned drow = 8u * (unsigned)wave + ((unsigned)lane >> 3);
@@ -183,10 +189,10 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
   }
 
   uint4 qc[kKlG][kKlNc];
-  load_q_tiles<bf16_t, kKlD, kKlG>(Q, qrow, kKlHq, g, lane, qc);
+  if (teacher) load_q_tiles<bf16_t, kKlD, kKlG>(Q, qrow, hq, g, lane, qc);
   // the tile's dense LSE (log2 units), read back per key tile
   float* biasl = reinterpret_cast<float*>(smem + kKlBias) + g * kKlG * 32 + col;
-  if (hf == 0) {
+  if (teacher && hf == 0) {
 #pragma unroll
     for (int h = 0; h < kKlG; ++h) biasl[32 * h] = lse[(size_t)(g * kKlG + h) * n + qrow] * kLog2e;
   }
@@ -216,39 +222,43 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
   for (int kt = 0; kt <= qt; ++kt) {
     const int k0 = kt << 5;
     const bool diag = kt == qt;
-    // ---- teacher: this wave's 4 heads, summed
-    uint4 kc[kKlNc];
-    wait_vmem_all();   // this wave's K tile (and k_idx piece) have landed
-    kl.read(slot, kc);
-    if (kt < qt) kl.issue(K, n, kKlHkv, g, (kt + 1) << 5, slot);
-    float pacc[16];
-    f32x16 a;
+    // ---- teacher: this wave's 4 heads, summed (waves of existing KV heads)
+    if (teacher) {
+      uint4 kc[kKlNc];
+      wait_vmem_all();   // this wave's K tile (and k_idx piece) have landed
+      kl.read(slot, kc);
+      if (kt < qt) kl.issue(K, n, hkv, g, (kt + 1) << 5, slot);
+      float pacc[16];
+      f32x16 a;
 #pragma unroll
-    for (int h = 0; h < kKlG; ++h) {
-      score_tile<bf16_t, kKlNc>(a, kc, qc[h]);
-      const float bias = biasl[32 * h];
+      for (int h = 0; h < kKlG; ++h) {
+        score_tile<bf16_t, kKlNc>(a, kc, qc[h]);
+        const float bias = biasl[32 * h];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(a[r], c, -bias));
-        pacc[r] = h == 0 ? e : pacc[r] + e;
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(a[r], c, -bias));
+          pacc[r] = h == 0 ? e : pacc[r] + e;
+        }
+        // one head at a time: keeps the scheduler from hoisting the next
+        // head's MFMAs (and their accumulators) above these exponentials
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // one head at a time: keeps the scheduler from hoisting the next
-      // head's MFMAs (and their accumulators) above these exponentials
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (diag) {
+      if (diag) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (acc_row(r, hf) > col) pacc[r] = 0.f;
-    }
-    {
-      const int wb = g * 1024 + lane;   // part_index(g, r, lane) = wb ^ (68 r)
+        for (int r = 0; r < 16; ++r)
+          if (acc_row(r, hf) > col) pacc[r] = 0.f;
+      }
+      {
+        const int wb = g * 1024 + lane;   // part_index(g, r, lane) = wb ^ (68 r)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part[wb ^ (68 * r)] = pacc[r];
+        for (int r = 0; r < 16; ++r) part[wb ^ (68 * r)] = pacc[r];
+      }
+    } else {
+      wait_vmem_all();   // this wave's k_idx piece has landed
     }
     barrier_lds();   // partial tiles visible
     if (wave < 4 && kt < qt) issue_kidx(kt + 1);
-    // ---- assemble P[key][query] = (1/Hq) sum over the 8 partial tiles
+    // ---- assemble P[key][query] = (1/Hq) sum over the hkv partial tiles
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = (int)threadIdx.x + 512 * u;
@@ -257,8 +267,8 @@ __global__ __launch_bounds__(512) void kl_tile_kernel(
       const int src = (r * 64 + ((qq + 32 * h2) ^ (4 * r)));
       float p = part[src];
 #pragma unroll
-      for (int gg = 1; gg < kKlHkv; ++gg) p += part[src + gg * 1024];
-      ptile[key * kKlPitch + qq] = p * (1.0f / (float)kKlHq);
+      for (int gg = 1; gg < hkv; ++gg) p += part[src + gg * 1024];
+      ptile[key * kKlPitch + qq] = p * inv_hq;
     }
     barrier_lds();   // P visible
     if (wave >= 2) continue;
@@ -391,15 +401,18 @@ __device__ __forceinline__ void dk_dma_piece(const bf16_t* X, int heads, int hea
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(slot + 1024 * c), 16, 0, 0);
 }
 
+template <int HKV>
 __global__ __launch_bounds__(512) void kl_dk_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ QI,
     const bf16_t* __restrict__ KI, const float* __restrict__ lse, const float* __restrict__ lse_t,
-    int n, float c, float ct, float* __restrict__ cpart) {
+    int n, float inv_hq, float c, float ct, float* __restrict__ cpart) {
+  constexpr int hkv = HKV;
   extern __shared__ __align__(1024) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hf = lane >> 5, col = lane & 31;
-  const int g = (int)(blockIdx.x % kKlHkv);          // XCD g serves group g
-  const int kb = (int)(blockIdx.x / kKlHkv);         // longest rows first
+  const int g = (int)(blockIdx.x % hkv);             // with 8 groups, XCD g serves group g
+  const int kb = (int)(blockIdx.x / hkv);            // longest rows first
+  const int hq = kKlG * hkv;
   const int ntiles = (n + 31) >> 5;
   const int kt = kb * kDkWaves + wave;               // this wave's key tile
   const int k0 = kt << 5;
@@ -410,9 +423,9 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
   uint4 kc[kKlNc];
   {
     KLane<bf16_t, kKlD> kl;
-    kl.init(lane, kKlHkv);
+    kl.init(lane, hkv);
     unsigned char* tmp = smem + 8192u * (unsigned)wave;
-    kl.issue(K, n, kKlHkv, g, min(k0, ((n - 1) >> 5) << 5), tmp);
+    kl.issue(K, n, hkv, g, min(k0, ((n - 1) >> 5) << 5), tmp);
     wait_vmem_all();
     kl.read(tmp, kc);
   }
@@ -442,7 +455,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
     const int hh = wave >> 1;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      dk_dma_piece(Q, kKlHq, g * kKlG + hh, q0, n, 4 * (wave & 1) + p, buf + kDkQ + 8192u * hh, lane);
+      dk_dma_piece(Q, hq, g * kKlG + hh, q0, n, 4 * (wave & 1) + p, buf + kDkQ + 8192u * hh, lane);
     if (wave < 4) {
       const int row = min(q0 + (int)drow, n - 1);
       const unsigned char* src = reinterpret_cast<const unsigned char*>(QI) + (size_t)row * (kKlDi * 2) + dpiece;
@@ -476,7 +489,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
     tr_off = 128u * (4u * (G16 >> 1) + e) + 8u * (cc & 1u) + 16u * (u ^ sw);
   }
   KLane<bf16_t, kKlD> ql;   // read offsets of the Q tiles (same layout as key tiles)
-  ql.init(lane, kKlHq);
+  ql.init(lane, hq);
 
   f32x16 cacc[2] = {f32x16{}, f32x16{}};   // C^T[32 dt + acc_row][key col]
   const bool active_wave = kt < ntiles;
@@ -517,7 +530,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
     // ---- v = (Q -) S/Hq on the live pairs (key <= query < n)
     float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = -psum[r] * (1.0f / (float)kKlHq);
+    for (int r = 0; r < 16; ++r) v[r] = -psum[r] * inv_hq;
     const uint32_t qb = base + kDkBuf * (unsigned)(qt & 1) + kDkQidx;
     if (g == 0) {
       f32x16 t = f32x16{};
@@ -573,16 +586,18 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(
   }
 }
 
-// dk[j][d] = grad_scale * sum over the 8 KV groups of C_g[j][d], in
+// dk[j][d] = grad_scale * sum over the hkv KV groups of C_g[j][d], in
 // increasing g.
+template <int HKV>
 __global__ __launch_bounds__(256) void kl_dk_sum_kernel(const float* __restrict__ cpart, int n,
                                                         float grad_scale, float* __restrict__ dk) {
+  constexpr int hkv = HKV;
   const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;   // 4 values of dk
   const size_t total = (size_t)n * kKlDi;
   if (e >= total) return;
   float4 a = *reinterpret_cast<const float4*>(cpart + e);
 #pragma unroll
-  for (int g = 1; g < kKlHkv; ++g) {
+  for (int g = 1; g < hkv; ++g) {
     const float4 x = *reinterpret_cast<const float4*>(cpart + (size_t)g * total + e);
     a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
   }
@@ -608,44 +623,64 @@ __global__ __launch_bounds__(256) void kl_loss_kernel(const float* __restrict__ 
 }  // namespace
 
 bool kl_shape_supported(const LayerShape& s, int d_idx) {
-  return s.dtype == kBF16 && s.d == kKlD && s.hkv == kKlHkv && s.hq == kKlHq && d_idx == kKlDi;
+  const bool hkv_ok = s.hkv == 1 || s.hkv == 2 || s.hkv == 4 || s.hkv == kKlHkv;
+  return s.dtype == kBF16 && s.d == kKlD && hkv_ok && s.hq == kKlG * s.hkv && d_idx == kKlDi;
 }
 
-size_t kl_partial_bytes(int n) { return (size_t)kKlHkv * (size_t)n * kKlDi * sizeof(float); }
+size_t kl_partial_bytes(int n, int hkv) { return (size_t)hkv * (size_t)n * kKlDi * sizeof(float); }
 
-hipError_t launch_kl_distill(const LayerShape& s, int d_idx, float idx_scale, const void* q,
-                             const void* k, const void* q_idx, const void* k_idx,
-                             const float* lse, const float* lse_t, float* kl_row, float* loss,
-                             float* dq, float* dk, float* dk_part, hipStream_t stream) {
-  if (!kl_shape_supported(s, d_idx)) return hipErrorInvalidValue;
+template <int HKV>
+static hipError_t run_kl_distill(const LayerShape& s, float idx_scale, const void* q,
+                                 const void* k, const void* q_idx, const void* k_idx,
+                                 const float* lse, const float* lse_t, float* kl_row, float* loss,
+                                 float* dq, float* dk, float* dk_part, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
   const float grad_scale = idx_scale / (float)s.n;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kl_tile_kernel),
+  const float inv_hq = 1.0f / (float)s.hq;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kl_tile_kernel<HKV>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kKlLds);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kl_dk_kernel),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kl_dk_kernel<HKV>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kl_tile_kernel, dim3(ntiles), dim3(512), kKlLds, stream,
+  hipLaunchKernelGGL(kl_tile_kernel<HKV>, dim3(ntiles), dim3(512), kKlLds, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_idx), lse,
-                     lse_t, s.n, s.scale * kLog2e, idx_scale * kLog2e, kl_row, dq, grad_scale);
+                     lse_t, s.n, inv_hq, s.scale * kLog2e, idx_scale * kLog2e, kl_row, dq,
+                     grad_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int kblocks = (ntiles + kDkWaves - 1) / kDkWaves;
-  hipLaunchKernelGGL(kl_dk_kernel, dim3(kblocks * kKlHkv), dim3(512), kDkLds, stream,
+  hipLaunchKernelGGL(kl_dk_kernel<HKV>, dim3(kblocks * HKV), dim3(512), kDkLds, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_idx), lse,
-                     lse_t, s.n, s.scale * kLog2e, idx_scale * kLog2e, dk_part);
+                     lse_t, s.n, inv_hq, s.scale * kLog2e, idx_scale * kLog2e, dk_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t quads = ((size_t)s.n * kKlDi + 3) / 4;
-  hipLaunchKernelGGL(kl_dk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream,
-                     dk_part, s.n, grad_scale, dk);
+  hipLaunchKernelGGL(kl_dk_sum_kernel<HKV>, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                     stream, dk_part, s.n, grad_scale, dk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (loss) {
     hipLaunchKernelGGL(kl_loss_kernel, dim3(1), dim3(256), 0, stream, kl_row, s.n, loss);
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_kl_distill(const LayerShape& s, int d_idx, float idx_scale, const void* q,
+                             const void* k, const void* q_idx, const void* k_idx,
+                             const float* lse, const float* lse_t, float* kl_row, float* loss,
+                             float* dq, float* dk, float* dk_part, hipStream_t stream) {
+  if (!kl_shape_supported(s, d_idx)) return hipErrorInvalidValue;
+#define AMTK_KL(H) \
+  run_kl_distill<H>(s, idx_scale, q, k, q_idx, k_idx, lse, lse_t, kl_row, loss, dq, dk, dk_part, stream)
+  switch (s.hkv) {
+    case 1: return AMTK_KL(1);
+    case 2: return AMTK_KL(2);
+    case 4: return AMTK_KL(4);
+    case 8: return AMTK_KL(8);
+  }
+#undef AMTK_KL
+  return hipErrorInvalidValue;
 }
 
 }  // namespace amtk

@@ -272,6 +272,14 @@ def test_kl_distill_validation(lib):
     need_big = ctypes.c_size_t(0)
     assert lib.amtk_kl_workspace(ctypes.byref(big), 64, ctypes.byref(need_big)) == 0
     assert need_big.value <= 100000 * (32 + 1 + 8 * 64) * 4 + 4096     # 218 MB at 100K
+    # 4 query heads per KV head with fewer KV heads: one key-gradient share per KV head
+    for hq, hkv in ((16, 4), (8, 2), (4, 1)):
+        c = _abi.AttnDesc(1000, hq, hkv, 128, _abi.AMTK_BF16, 1, 0.0)
+        assert lib.amtk_kl_workspace(ctypes.byref(c), 64, ctypes.byref(need)) == 0
+        assert 1000 * (hq + 1 + hkv * 64) * 4 <= need.value <= 1000 * (hq + 1 + hkv * 64) * 4 + 4096
+    for hq, hkv in ((16, 8), (32, 4), (8, 8)):   # other group sizes: not covered
+        c = _abi.AttnDesc(1000, hq, hkv, 128, _abi.AMTK_BF16, 1, 0.0)
+        assert lib.amtk_kl_workspace(ctypes.byref(c), 64, ctypes.byref(need)) == -2
     f = lib.kl_distill
     args = [FAKE] * 8
     assert f(ctypes.byref(b), 64, 0.0, *args, FAKE, need.value - 1, None) == -3

@@ -119,6 +119,32 @@ def test_kl_distill_small_shapes_every_row_and_key(gpu_lib, n):
     _check_properties(kl, loss, dq, dk, qi, ki, kd.scale)
 
 
+@pytest.mark.parametrize("n,hq,hkv", [
+    (100, 16, 4),   # 4 KV heads: 4 of the tile kernel's 8 waves score the teacher
+    (161, 8, 2),
+    (70, 4, 1),     # one KV head (MQA-style groups of 4)
+    (33, 8, 2),     # a ragged second tile
+])
+def test_kl_distill_other_head_layouts_every_row_and_key(gpu_lib, n, hq, hkv):
+    """4 query heads per KV head with 1, 2 or 4 KV heads: every row and key
+    against the oracle, the loss, and the gradient identities."""
+    import torch
+    x = random_inputs(n, hq, hkv, 128, "bf16", seed=500 + n + hkv, sink=True)
+    qi, ki = _idx_inputs(n, 600 + n + hkv)
+    t = _upload(x, qi, ki)
+    kl, loss, dq, dk = _run(gpu_lib, t)
+    kd = KLDistillOracle(OracleLayer(x["q"], x["k"], x["v"]), qi, ki)
+    _check_rows(kd, range(n), kl, dq, qi, ki)
+    _check_keys(kd, list(range(n)), dk, qi)
+    full = kd.full()
+    assert abs(loss - full["loss"]) <= 1e-4 * max(1.0, abs(full["loss"]))
+    _check_properties(kl, loss, dq, dk, qi, ki, kd.scale)
+    again = gpu_lib.kl_distill(t["q"], t["k"], t["qi"], t["ki"])   # deterministic
+    torch.cuda.synchronize()
+    for a, b in zip(again, (kl, np.array([loss], dtype=np.float32), dq, dk)):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
 def test_kl_distill_student_equals_teacher_gives_zero(gpu_lib):
     """Four identical query heads per KV head and identical KV heads make the
     head-averaged mass one head's softmax; with q_idx, k_idx the first 64
