@@ -6,10 +6,12 @@
 // (token ids, or 64-token key blocks from the indexer); the softmax is taken
 // over the support only. The abstract states the same recompute step.
 //
-// Three attention kernels. bf16 with d = 128 and 8 KV heads x 4 query heads
-// runs on MFMAs (sparse_attn_mfma_kernel, near the end of this file), in one
-// pass or in key windows (support_windows_kernel finds where each window
-// starts in every row's support; the windowed gather closes the file). The other
+// Three attention kernels. bf16 with d = 128, 1, 2, 4 or 8 query heads per
+// KV head and a power-of-two number of KV heads runs on MFMAs
+// (sparse_attn_mfma_kernel, near the end of this file), in one pass or in key
+// windows (support_windows_kernel finds where each window starts in every
+// row's support; the windowed gather closes the file); the rows of a
+// selection block may all read the block's first index row. The other
 // shapes use one wavefront per query row, rows issued longest first: all Hq
 // heads share the row's support, so one gathered token row K[j] (all Hkv
 // heads, d contiguous: Hkv*d elements) serves every head. In the generic
@@ -187,8 +189,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Fast path for bf16, d = 128, 8 KV heads x 4 query heads each (the shape of
-// the long-context GQA layers). One wave per query row; lane l serves KV head
+// VALU path for bf16, d = 128, 8 KV heads x 4 query heads each (the shape of
+// the long-context GQA layers) where the MFMA path does not apply (token rows
+// of all KV heads beyond 32-bit byte offsets). One wave per query row; lane l serves KV head
 // g = l/8 and the 16 elements d in [16*(l%8), 16*(l%8)+16) of the K/V rows.
 //  * QK: v_dot2 on raw bf16 pairs (no conversion), 8 per head and token.
 //  * The 8 lanes of a KV head finish its 4 logits with a transposed DPP
@@ -368,12 +371,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_g4_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path for bf16, d = 128, 8 KV heads x 4 query heads, key blocks of 1
-// or a multiple of 16 tokens. One single-wave workgroup per (query row, KV
-// head), numbered row-major with the KV head fastest: workgroups are handed
-// to the 8 XCDs round robin, so XCD g serves KV head g of every row and its
+// MFMA path for bf16, d = 128, G = 1, 2, 4 or 8 query heads per KV head and
+// a power-of-two number of KV heads, key blocks of 1 or a multiple of 16
+// tokens. One single-wave workgroup per (query row, KV head), numbered
+// row-major with the KV head fastest: workgroups are handed to the 8 XCDs
+// round robin, so with 8 KV heads XCD g serves KV head g of every row and its
 // L2 holds the keys and values of that one head (an eighth of the layer).
-// The support is walked in chunks of 32 tokens; a chunk is two sets of 16
+// The support is walked in chunks of 32 tokens (16 for short or key-block
+// supports: one set); a chunk is two sets of 16
 // (sigma = 0, 1), MFMA row m of set sigma being token 16*sigma + m.
 //  * every global read of the loop is a DMA into LDS (no registers, no ALU
 //    work): instruction c of a chunk brings the whole 256-byte key (and

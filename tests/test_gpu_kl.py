@@ -124,6 +124,7 @@ def test_kl_distill_small_shapes_every_row_and_key(gpu_lib, n):
     (161, 8, 2),
     (70, 4, 1),     # one KV head (MQA-style groups of 4)
     (33, 8, 2),     # a ragged second tile
+    (600, 16, 4),   # three 256-key blocks of the key-gradient kernel, the last partial
 ])
 def test_kl_distill_other_head_layouts_every_row_and_key(gpu_lib, n, hq, hkv):
     """4 query heads per KV head with 1, 2 or 4 KV heads: every row and key
