@@ -25,7 +25,8 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
-    "pass1_lse": "sparse_long_context_causal_amd/csrc/passes.hip",
+    "pass1_lse": ("sparse_long_context_causal_amd/csrc/passes.hip",
+                  "sparse_long_context_causal_amd/csrc/pass1_direct.hip"),
     "pass2_filter": "sparse_long_context_causal_amd/csrc/passes.hip",
     "select": "sparse_long_context_causal_amd/csrc/select.hip",
     "sparse_attn": "sparse_long_context_causal_amd/csrc/sparse_attn.hip",
@@ -41,7 +42,8 @@ def log(*a):
 
 def source_hash(rel):
     h = hashlib.sha256()
-    h.update(open(os.path.join(ROOT, rel), "rb").read())
+    for r in ((rel,) if isinstance(rel, str) else rel):
+        h.update(open(os.path.join(ROOT, r), "rb").read())
     h.update(open(os.path.join(ROOT, "sparse_long_context_causal_amd/csrc/device_common.h"),
                   "rb").read())
     return h.hexdigest()[:16]

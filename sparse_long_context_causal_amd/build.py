@@ -29,6 +29,12 @@ CFLAGS = [
 ]
 
 
+# Per-file flags. pass1_direct.hip: MFMA results in vector registers (its
+# kernel may use the accumulation registers, where the compiler would
+# otherwise put the results and copy each one out for the VALU).
+FILE_FLAGS = {"pass1_direct.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc():
     for c in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"), "hipcc"):
         if os.path.sep not in c or os.path.exists(c):
@@ -39,7 +45,7 @@ def _hipcc():
 def _compile(src):
     sub = "calib_" if os.path.dirname(src) == CALIB_SRC else ""
     obj = os.path.join(OBJ, sub + os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -161,9 +161,11 @@ int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const 
       e = amtk::launch_block_topk(s, sp.query_block, sp.k, colsum, idx, count, mass, stream);
     return e == hipSuccess ? AMTK_OK : hip_fail(e);
   }
-  const CandidatePool pool = pool_of(ws, L);
+  CandidatePool pool = pool_of(ws, L);
+  // a whole call: pass 2 reads the keys pass 1 copied into operand order
+  pool.kops_ready = stage == 0 && pool.kops && amtk::pass1_writes_kops(s) && sp.key_block == 1;
   if (stage == 0 || stage == 1) {
-    e = amtk::launch_pass1_lse(s, q, k, lse_buf, pool.ovf_count, stream);
+    e = amtk::launch_pass1_lse_kops(s, q, k, lse_buf, pool.ovf_count, pool.kops, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (stage == 0 || stage == 2) {

@@ -32,6 +32,7 @@ struct CandidatePool {
   void* kops;       // key tiles in MFMA operand order (pass2_key_operand_bytes)
   int cap;          // capacity per row
   int slots;        // overflow rows processed concurrently
+  bool kops_ready = false;   // kops already holds this call's keys (written by pass 1)
 };
 
 constexpr int kMaxBudget = 8192;      // largest k the select kernel sorts in LDS
@@ -48,6 +49,17 @@ size_t pass2_key_operand_bytes(const LayerShape& s, int key_block);
 // pool.ovf_count for the pass that follows.
 hipError_t launch_pass1_lse(const LayerShape& s, const void* q, const void* k, float* lse,
                             int* zero_counter, hipStream_t stream);
+// The same for bf16, d = 128, 8 KV heads x 4 query heads with a workspace of
+// pass2_key_operand_bytes(s, 1) at kops: the keys are copied there in MFMA
+// operand order, and pass 1 reads them straight into registers. Other shapes
+// (or kops == nullptr) run launch_pass1_lse.
+hipError_t launch_pass1_lse_kops(const LayerShape& s, const void* q, const void* k, float* lse,
+                                 int* zero_counter, void* kops, hipStream_t stream);
+// Whether launch_pass1_lse_kops takes the direct path (and so writes kops).
+bool pass1_writes_kops(const LayerShape& s);
+// The pass-1 kernel of launch_pass1_lse_kops alone (kops already written).
+hipError_t launch_pass1_direct(const LayerShape& s, const void* q, const void* kops, float* lse,
+                               int* zero_counter, hipStream_t stream);
 
 // Head-averaged mass, streaming threshold filter, candidate compaction.
 hipError_t launch_pass2_filter(const LayerShape& s, int key_block, int budget, const void* q,

@@ -1053,8 +1053,9 @@ static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, cons
     kops = static_cast<uint4*>(pool.kops);
     if (!kops) return hipErrorInvalidValue;
     const size_t total = (size_t)8 * ntiles * 512;
-    hipLaunchKernelGGL(key_operands_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, static_cast<const bf16_t*>(k), kops, s.n, ntiles);
+    if (!pool.kops_ready)
+      hipLaunchKernelGGL(key_operands_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<const bf16_t*>(k), kops, s.n, ntiles);
   }
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
@@ -1128,6 +1129,27 @@ bool pass_shape_supported(const LayerShape& s) {
     }                                                                                \
     return hipErrorInvalidValue;                                                     \
   } while (0)
+
+#ifndef AMTK_P1_DIRECT
+#define AMTK_P1_DIRECT 1
+#endif
+
+bool pass1_writes_kops(const LayerShape& s) {
+  // the direct kernel's shape: bf16, d = 128, 8 KV heads x 4 query heads
+  return AMTK_P1_DIRECT && pass2_key_operand_bytes(s, 1) != 0 && s.hq == 4 * s.hkv;
+}
+
+hipError_t launch_pass1_lse_kops(const LayerShape& s, const void* q, const void* k, float* lse,
+                                 int* zero_counter, void* kops, hipStream_t stream) {
+  if (!kops || !pass1_writes_kops(s)) return launch_pass1_lse(s, q, k, lse, zero_counter, stream);
+  const int ntiles = (s.n + 31) / 32;
+  const size_t total = (size_t)8 * ntiles * 512;
+  hipLaunchKernelGGL(key_operands_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const bf16_t*>(k), static_cast<uint4*>(kops), s.n, ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_pass1_direct(s, q, kops, lse, zero_counter, stream);
+}
 
 hipError_t launch_pass1_lse(const LayerShape& s, const void* q, const void* k, float* lse,
                             int* zero_counter, hipStream_t stream) {
