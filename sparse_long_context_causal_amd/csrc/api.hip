@@ -81,6 +81,10 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
     // per selection block without them)
     const size_t cs = sp.key_block == 1 ? (n + 31) / 32 * n * sizeof(float) : 0;
     L.colsum = off;  off = round_up(off + cs);
+    // pass 1 reads the keys from a copy in MFMA operand order where it can
+    L.kops_bytes = sp.key_block == 1 && amtk::pass1_writes_kops(s)
+                       ? amtk::pass2_key_operand_bytes(s, 1) : 0;
+    L.kops = off;    off = round_up(off + L.kops_bytes);
     L.total = off;
     return L;
   }
@@ -154,7 +158,8 @@ int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const 
   if (sp.query_block != 1) {   // one support per selection block of consecutive queries
     float* colsum = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + L.colsum);
     int* zero = reinterpret_cast<int*>(static_cast<unsigned char*>(ws) + L.ovf_count);
-    if (stage == 0 || stage == 1) e = amtk::launch_pass1_lse(s, q, k, lse_buf, zero, stream);
+    void* kops = L.kops_bytes ? static_cast<unsigned char*>(ws) + L.kops : nullptr;
+    if (stage == 0 || stage == 1) e = amtk::launch_pass1_lse_kops(s, q, k, lse_buf, zero, kops, stream);
     if (e == hipSuccess && (stage == 0 || stage == 2))
       e = amtk::launch_pass2_colsum(s, q, k, lse_buf, colsum, stream);
     if (e == hipSuccess && (stage == 0 || stage == 3))

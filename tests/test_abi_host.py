@@ -136,6 +136,13 @@ def test_selection_block_workspace_and_pool_stats(lib):
     assert lib.amtk_topk_workspace(ctypes.byref(a), ctypes.byref(s), ctypes.byref(need)) == 0
     assert need.value >= (n + 31) // 32 * n * 4 + hq * n * 4
     assert need.value < (n + 31) // 32 * n * 4 + hq * n * 4 + 4096
+    # bf16, d = 128, 32/8 heads: plus pass 1's copy of K in MFMA operand order
+    from sparse_long_context_causal_amd import _abi
+    b = _abi.AttnDesc(n, 32, 8, 128, _abi.AMTK_BF16, 1, 0.0)
+    need_b = ctypes.c_size_t(0)
+    assert lib.amtk_topk_workspace(ctypes.byref(b), ctypes.byref(s), ctypes.byref(need_b)) == 0
+    base = (n + 31) // 32 * n * 4 + 32 * n * 4 + (n + 31) // 32 * 32 * 8 * 128 * 2
+    assert base <= need_b.value < base + 4096
     z = ctypes.c_int64(0)
     assert lib.amtk_pool_stats(ctypes.byref(a), ctypes.byref(s), FAKE, need.value, ctypes.byref(z),
                                ctypes.byref(z), ctypes.byref(z), None) == -2
