@@ -347,7 +347,7 @@ int amtk_kl_workspace(const amtk_attn_desc* attn, int32_t d_idx, size_t* bytes);
  *   dk_idx[j] = dloss/dk_idx[j] = (idx_scale/n) sum_{i>=j} (Q_ij - P_ij) q_idx[i]
  * No n x n matrix, and no array of that size, is stored: the workspace is
  * O(n * (hq + hkv * d_idx)) floats (the dense LSE, the student LSE and the
- * key gradient's per-KV-group shares). Both gradients are deterministic
+ * key gradient's per-KV-group shares) plus, for 32/8 heads, a copy of K. Both gradients are deterministic
  * (fixed summation order).
  * q, k      : as for topk_support; bf16, d = 128, 4 query heads per KV head
  *             and 1, 2, 4 or 8 KV heads (hq = 4 * hkv); anything else returns
@@ -356,8 +356,10 @@ int amtk_kl_workspace(const amtk_attn_desc* attn, int32_t d_idx, size_t* bytes);
  * kl_row    : OUT [n] fp32.   loss: OUT [1] fp32, or NULL.
  * dq_idx    : OUT [n][d_idx] fp32.   dk_idx: OUT [n][d_idx] fp32.
  * ws        : device workspace of ws_bytes >= amtk_kl_workspace()
- *             (n * (hq + 1 + hkv * d_idx) * 4 bytes plus alignment: 71 MB at
- *             n = 32768 with 32/8 heads).
+ *             (n * (hq + 1 + hkv * d_idx) * 4 bytes, with 8 KV heads x 4
+ *             query heads plus a copy of K in MFMA operand order for the
+ *             teacher's LSE pass, plus alignment: 138 MB at n = 32768 with
+ *             32/8 heads).
  */
 int kl_distill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale, const void* q,
                const void* k, const void* q_idx, const void* k_idx, float* kl_row, float* loss,

@@ -409,7 +409,7 @@ int support_overlap(int64_t n, int32_t max_a, const int32_t* idx_a, const int32_
 namespace {
 
 struct KlLayout {
-  size_t lse, lse_t, zero, part, total;
+  size_t lse, lse_t, zero, part, kops, kops_bytes, total;
 };
 
 KlLayout kl_layout(const LayerShape& s) {
@@ -419,6 +419,10 @@ KlLayout kl_layout(const LayerShape& s) {
   L.lse_t = off;  off = round_up(off + (size_t)s.n * sizeof(float));
   L.zero = off;   off = round_up(off + sizeof(int));
   L.part = off;   off = round_up(off + amtk::kl_partial_bytes(s.n, s.hkv));
+  // the teacher's LSE pass reads the keys from a copy in MFMA operand order
+  // where it can
+  L.kops_bytes = amtk::pass1_writes_kops(s) ? amtk::pass2_key_operand_bytes(s, 1) : 0;
+  L.kops = off;   off = round_up(off + L.kops_bytes);
   L.total = off;
   return L;
 }
@@ -466,7 +470,8 @@ int kl_distill(const amtk_attn_desc* attn, int32_t d_idx, float idx_scale, const
   int* zero = reinterpret_cast<int*>(w + L.zero);
   si.scale = idx_scale > 0.f ? idx_scale : 1.0f / std::sqrt((float)d_idx);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = amtk::launch_pass1_lse(s, q, k, lse, zero, st);
+  void* kops = L.kops_bytes ? w + L.kops : nullptr;
+  hipError_t e = amtk::launch_pass1_lse_kops(s, q, k, lse, zero, kops, st);
   if (e == hipSuccess) e = amtk::launch_pass1_lse(si, q_idx, k_idx, lse_t, zero, st);
   if (e == hipSuccess)
     e = amtk::launch_kl_distill(s, d_idx, si.scale, q, k, q_idx, k_idx, lse, lse_t, kl_row, loss,
