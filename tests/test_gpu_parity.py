@@ -161,19 +161,23 @@ def test_key_classes_exact_supports(gpu_lib, n, k, probs):
         assert res["idx"][i][: len(want)].tolist() == want, f"row {i}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_lse_far_above_first_key_tile(gpu_lib, dtype):
+@pytest.mark.parametrize("dtype,hq,hkv,d", [
+    ("f32", 8, 2, 64),
+    ("bf16", 8, 2, 64),
+    ("bf16", 32, 8, 128),   # pass 1 from the keys in operand order (its redo path)
+])
+def test_lse_far_above_first_key_tile(gpu_lib, dtype, hq, hkv, d):
     """One key (id 100) scores about 180 log2 units above every key of the
     first 32-key tile, so a sum referenced to the first tile's maximum would
     overflow; rows that see it must still match the oracle (their LSE is
     about 125, so fp32 keeps ~1e-5 there: the check allows 4 ulp on top)."""
-    n, hq, hkv, d = 200, 8, 2, 64
+    n = 200
     rng = np.random.default_rng(77)
     e0 = np.zeros(d)
     e0[0] = 1.0
     q = (25.0 * e0 + 0.01 * rng.standard_normal((n, hq, d))).astype(np.float32)
     k = rng.standard_normal((n, hkv, d)).astype(np.float32)
-    k[100] = 40.0 * e0
+    k[100] = 40.0 * math.sqrt(d / 64) * e0   # the same logit, 125 (180 log2 units), at any d
     v = rng.standard_normal((n, hkv, d)).astype(np.float32)
     if dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
