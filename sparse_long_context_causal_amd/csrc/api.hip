@@ -4,6 +4,7 @@
 // workspace, and enqueues the kernels on the caller's stream. Nothing here
 // allocates device memory or synchronises (except amtk_pool_stats, which is
 // documented as a synchronous diagnostic).
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -82,8 +83,7 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
     const size_t cs = sp.key_block == 1 ? (n + 31) / 32 * n * sizeof(float) : 0;
     L.colsum = off;  off = round_up(off + cs);
     // pass 1 reads the keys from a copy in MFMA operand order where it can
-    L.kops_bytes = sp.key_block == 1 && amtk::pass1_writes_kops(s)
-                       ? amtk::pass2_key_operand_bytes(s, 1) : 0;
+    L.kops_bytes = sp.key_block == 1 ? amtk::pass1_key_operand_bytes(s) : 0;
     L.kops = off;    off = round_up(off + L.kops_bytes);
     L.total = off;
     return L;
@@ -102,7 +102,10 @@ Layout layout(const LayerShape& s, const amtk_support_desc& sp) {
   L.ovf_count = off;  off = round_up(off + sizeof(int));
   L.ovf_list = off;   off = round_up(off + n * sizeof(int));
   L.scratch = off;    off = round_up(off + (size_t)amtk::kFallbackSlots * L.units_max * sizeof(float));
-  L.kops_bytes = amtk::pass2_key_operand_bytes(s, sp.key_block);
+  // the keys in MFMA operand order: pass 1's copy, which pass 2 also reads
+  // with 8 KV heads and token units (the same layout)
+  L.kops_bytes = std::max(amtk::pass1_key_operand_bytes(s),
+                          amtk::pass2_key_operand_bytes(s, sp.key_block));
   L.kops = off;       off = round_up(off + L.kops_bytes);
   L.colsum = 0;
   L.total = off;
@@ -168,7 +171,8 @@ int run_topk(const LayerShape& s, const amtk_support_desc& sp, int stage, const 
   }
   CandidatePool pool = pool_of(ws, L);
   // a whole call: pass 2 reads the keys pass 1 copied into operand order
-  pool.kops_ready = stage == 0 && pool.kops && amtk::pass1_writes_kops(s) && sp.key_block == 1;
+  pool.kops_ready = stage == 0 && pool.kops && amtk::pass1_writes_kops(s) &&
+                    amtk::pass2_key_operand_bytes(s, sp.key_block) != 0;
   if (stage == 0 || stage == 1) {
     e = amtk::launch_pass1_lse_kops(s, q, k, lse_buf, pool.ovf_count, pool.kops, stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -421,7 +425,7 @@ KlLayout kl_layout(const LayerShape& s) {
   L.part = off;   off = round_up(off + amtk::kl_partial_bytes(s.n, s.hkv));
   // the teacher's LSE pass reads the keys from a copy in MFMA operand order
   // where it can
-  L.kops_bytes = amtk::pass1_writes_kops(s) ? amtk::pass2_key_operand_bytes(s, 1) : 0;
+  L.kops_bytes = amtk::pass1_key_operand_bytes(s);
   L.kops = off;   off = round_up(off + L.kops_bytes);
   L.total = off;
   return L;

@@ -49,14 +49,17 @@ size_t pass2_key_operand_bytes(const LayerShape& s, int key_block);
 // pool.ovf_count for the pass that follows.
 hipError_t launch_pass1_lse(const LayerShape& s, const void* q, const void* k, float* lse,
                             int* zero_counter, hipStream_t stream);
-// The same for bf16, d = 128, 8 KV heads x 4 query heads with a workspace of
-// pass2_key_operand_bytes(s, 1) at kops: the keys are copied there in MFMA
-// operand order, and pass 1 reads them straight into registers. Other shapes
-// (or kops == nullptr) run launch_pass1_lse.
+// The same for bf16, d = 128, 1, 2, 4 or 8 KV heads and 2 or 4 query heads
+// per KV head with a workspace of pass1_key_operand_bytes(s) at kops: the
+// keys are copied there in MFMA operand order, and pass 1 reads them
+// straight into registers. Other shapes (or kops == nullptr) run
+// launch_pass1_lse.
 hipError_t launch_pass1_lse_kops(const LayerShape& s, const void* q, const void* k, float* lse,
                                  int* zero_counter, void* kops, hipStream_t stream);
-// Whether launch_pass1_lse_kops takes the direct path (and so writes kops).
+// Whether launch_pass1_lse_kops takes the direct path (and so writes kops),
+// and the bytes of kops it then needs.
 bool pass1_writes_kops(const LayerShape& s);
+size_t pass1_key_operand_bytes(const LayerShape& s);
 // The pass-1 kernel of launch_pass1_lse_kops alone (kops already written).
 hipError_t launch_pass1_direct(const LayerShape& s, const void* q, const void* kops, float* lse,
                                int* zero_counter, hipStream_t stream);

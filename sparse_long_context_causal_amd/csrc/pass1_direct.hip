@@ -1,6 +1,6 @@
 // Pass 1 (per-head row log-sum-exp) reading the key tiles from a copy in
 // MFMA operand order (written by key_operands_kernel in passes.hip), for
-// bf16, d = 128 and 4 query heads per KV head.
+// bf16, d = 128 and 2 or 4 query heads per KV head.
 //
 // Method: "How Much Dense Attention is Necessary? Oracle-Guided Sparse
 // Prefill for Full/GQA Layers in Hybrid Long-Context Models" (arXiv
@@ -21,7 +21,7 @@
 namespace amtk {
 
 // ------------------------------------- pass 1 from the operand-order keys
-// bf16, d = 128, 4 query heads per KV head, with the key tiles already in
+// bf16, d = 128, 2 or 4 query heads per KV head, with the key tiles already in
 // MFMA operand order (key_operands_kernel). One wave per (32-row
 // tile, KV head) and no LDS: key tiles come from memory straight into
 // registers, a ring of kP1Ring tiles ahead of the one in use, which the
@@ -34,18 +34,21 @@ namespace amtk {
 #endif
 constexpr int kP1Ring = AMTK_P1_RING;
 static_assert(kP1Ring == 2 || kP1Ring == 3, "ring of 2 or 3 key tiles");
+template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 pass1_lse_direct_kernel(const bf16_t* __restrict__ Q, const uint4* __restrict__ kops,
                         float* __restrict__ lse, int n, int hkv, float c, float tau,
                         int* __restrict__ zero_counter) {
   typedef bf16_t T;
-  constexpr int D = 128, G = 4, NC = KTile<T, D>::kChunks;
+  constexpr int D = 128, NC = KTile<T, D>::kChunks;
   static_assert(NC == 8, "8 chunks of 16 bytes per lane and key tile");
+  static_assert(G == 2 || G == 4, "an even number of query heads per KV head (interleaved heads)");
   const int lane = threadIdx.x;
   const int hf = lane >> 5, col = lane & 31;
   const int ntiles = (n + 31) >> 5;
   const int qt = ntiles - 1 - (int)(blockIdx.x / (unsigned)hkv);   // longest rows first
   const int g = (int)(blockIdx.x % (unsigned)hkv);   // (8 KV heads: XCD g serves head g)
+  // (the kernel takes the KV head count at run time: a power of two up to 8)
   const int q0 = qt << 5;
   const int hq = hkv * G;
   if (blockIdx.x == 0 && lane == 0 && zero_counter) *zero_counter = 0;
@@ -236,7 +239,8 @@ pass1_lse_direct_kernel(const bf16_t* __restrict__ Q, const uint4* __restrict__ 
 hipError_t launch_pass1_direct(const LayerShape& s, const void* q, const void* kops, float* lse,
                                int* zero_counter, hipStream_t stream) {
   const int ntiles = (s.n + 31) / 32;
-  hipLaunchKernelGGL(pass1_lse_direct_kernel, dim3((unsigned)(ntiles * s.hkv)), dim3(64), 0, stream,
+  auto kern = s.hq == 2 * s.hkv ? pass1_lse_direct_kernel<2> : pass1_lse_direct_kernel<4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(ntiles * s.hkv)), dim3(64), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const uint4*>(kops), lse, s.n,
                      s.hkv, s.scale * kLog2e, s.scale, zero_counter);
   return hipGetLastError();

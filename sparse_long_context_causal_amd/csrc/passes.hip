@@ -988,21 +988,21 @@ __global__ __launch_bounds__(512) void pass2_filter_kernel(
   }
 }
 
-// Key tiles in MFMA operand order (8 KV heads, bf16, d = 128): entry
+// Key tiles in MFMA operand order (hkv KV heads, bf16, d = 128): entry
 // ((g * T + t) * 8 + c) * 64 + l is the 16-byte chunk c of lane l's operand
 // of tile t of KV head g, i.e. K[32 t + l % 32][g][64 (l / 32) + 8 c ..]
 // (rows past n repeat row n - 1), so a wave loads one tile as 8 fully
 // contiguous 1 KiB reads.
 __global__ __launch_bounds__(256) void key_operands_kernel(const bf16_t* __restrict__ K,
                                                            uint4* __restrict__ kops, int n,
-                                                           int ntiles) {
+                                                           int ntiles, int hkv) {
   const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= (size_t)8 * ntiles * 512) return;
+  if (id >= (size_t)hkv * ntiles * 512) return;
   const int l = (int)(id & 63), c = (int)((id >> 6) & 7);
   const size_t gt = id >> 9;
   const int t = (int)(gt % (size_t)ntiles), g = (int)(gt / (size_t)ntiles);
   const int row = min(t * 32 + (l & 31), n - 1);
-  kops[id] = *reinterpret_cast<const uint4*>(K + ((size_t)row * 8 + g) * 128 + 64 * (l >> 5) + 8 * c);
+  kops[id] = *reinterpret_cast<const uint4*>(K + ((size_t)row * hkv + g) * 128 + 64 * (l >> 5) + 8 * c);
 }
 
 // ------------------------------------------------------------ dispatching
@@ -1055,7 +1055,7 @@ static hipError_t run_pass2(const LayerShape& s, int budget, const void* q, cons
     const size_t total = (size_t)8 * ntiles * 512;
     if (!pool.kops_ready)
       hipLaunchKernelGGL(key_operands_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                         stream, static_cast<const bf16_t*>(k), kops, s.n, ntiles);
+                         stream, static_cast<const bf16_t*>(k), kops, s.n, ntiles, 8);
   }
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(64 * s.hkv), lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), lse, s.n, s.hkv,
@@ -1135,17 +1135,26 @@ bool pass_shape_supported(const LayerShape& s) {
 #endif
 
 bool pass1_writes_kops(const LayerShape& s) {
-  // the direct kernel's shape: bf16, d = 128, 8 KV heads x 4 query heads
-  return AMTK_P1_DIRECT && pass2_key_operand_bytes(s, 1) != 0 && s.hq == 4 * s.hkv;
+  // the direct kernel's shapes: bf16, d = 128, 1, 2, 4 or 8 KV heads, 2 or 4
+  // query heads per KV head
+  if (!AMTK_P1_DIRECT || s.dtype != kBF16 || s.d != 128) return false;
+  if (s.hkv != 1 && s.hkv != 2 && s.hkv != 4 && s.hkv != 8) return false;
+  return s.hq == 2 * s.hkv || s.hq == 4 * s.hkv;
+}
+
+size_t pass1_key_operand_bytes(const LayerShape& s) {
+  if (!pass1_writes_kops(s)) return 0;
+  return (size_t)((s.n + 31) / 32) * 32 * s.hkv * 128 * sizeof(bf16_t);
 }
 
 hipError_t launch_pass1_lse_kops(const LayerShape& s, const void* q, const void* k, float* lse,
                                  int* zero_counter, void* kops, hipStream_t stream) {
   if (!kops || !pass1_writes_kops(s)) return launch_pass1_lse(s, q, k, lse, zero_counter, stream);
   const int ntiles = (s.n + 31) / 32;
-  const size_t total = (size_t)8 * ntiles * 512;
+  const size_t total = (size_t)s.hkv * ntiles * 512;
   hipLaunchKernelGGL(key_operands_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, static_cast<const bf16_t*>(k), static_cast<uint4*>(kops), s.n, ntiles);
+                     stream, static_cast<const bf16_t*>(k), static_cast<uint4*>(kops), s.n, ntiles,
+                     s.hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_pass1_direct(s, q, kops, lse, zero_counter, stream);
